@@ -1,0 +1,65 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 storage conversions,
+// MFMA operand types, order-preserving float keys and launch wrappers'
+// declarations.  Host validation lives in dsv4_api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsv4 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// bf16 bits -> float (exact).
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bf16 bits, round to nearest, ties to even.  NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Two floats -> packed bf16x2 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16_bits(a)) |
+         (static_cast<uint32_t>(f32_to_bf16_bits(b)) << 16);
+}
+
+// Order-preserving unsigned key of a float: a < b  <=>  key(a) < key(b) for
+// non-NaN inputs; -0 and +0 map to the same key.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;  // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Pooled rows visible to a query at absolute position p (ratio 4).
+__device__ __forceinline__ int64_t visible_rows(int64_t p) { return (p + 1) >> 2; }
+
+}  // namespace dsv4
+
+// Launch wrappers (defined next to their kernels).  All return hipError_t of
+// the launch; argument checks happen before they are called.
+hipError_t dsv4_launch_compress(void* rows, void* rem, int64_t n_rows, int32_t n_rem,
+                                int32_t dim, int32_t dtype, const void* x, int64_t n_new,
+                                hipStream_t s);
+hipError_t dsv4_launch_fill_sequential(int32_t* out, int64_t T, int64_t q_pos0, int64_t S,
+                                       int32_t topk, hipStream_t s);
+hipError_t dsv4_launch_indexer_scores(const void* q, const float* w, const void* keys,
+                                      int64_t rows, int64_t q_pos0, int64_t S, int32_t n_heads,
+                                      int32_t dim, int32_t fold_mask, float* out,
+                                      int64_t out_stride, hipStream_t s);
+hipError_t dsv4_launch_topk(const float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
+                            int32_t topk, int32_t* out_idx, hipStream_t s);
+hipError_t dsv4_launch_sparse_attn(const void* q, int64_t T, int64_t q_pos0, int32_t n_heads,
+                                   int32_t head_dim, float scale, const void* raw_kv,
+                                   int64_t raw_pos0, int32_t window, const void* pooled,
+                                   const int32_t* sel_idx, int32_t topk, void* out,
+                                   hipStream_t s);

@@ -1,0 +1,121 @@
+"""Host-only checks of the C-ABI library: it loads, exports every function
+include/dsv4.h declares, and rejects bad arguments on the host before
+anything touches HIP (every call below fails validation or needs no device;
+none enqueues work)."""
+import ctypes
+
+import pytest
+
+import sparse_indexed_attention_amd as dsv4
+from sparse_indexed_attention_amd import dsv4_pool_cache
+
+OK, INVALID, UNSUPPORTED, CAPACITY, MISMATCH, SCRATCH = 0, -1, -2, -3, -4, -5
+FAKE = 0x1000  # never dereferenced: every call using it fails validation first
+
+
+def test_library_exports_every_header_function():
+    L = dsv4.lib()
+    names = dsv4.header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(dsv4._SIGNATURES)
+
+
+def test_abi_version_and_host_helpers():
+    assert dsv4.dsv4_abi_version() == 1
+    assert dsv4.dsv4_indexer_all_pooled(0, 8) is False
+    assert dsv4.dsv4_indexer_all_pooled(1, 8) is True
+    assert dsv4.dsv4_indexer_all_pooled(8, 8) is True
+    assert dsv4.dsv4_indexer_all_pooled(9, 8) is False
+    assert dsv4.dsv4_score_stride(1) == 64 and dsv4.dsv4_score_stride(64) == 64
+    assert dsv4.dsv4_score_stride(65) == 128
+    # one 1,024-row tile against 262,144 pooled rows: 1 GiB of fp32 scores
+    assert dsv4.dsv4_indexer_scratch_bytes(1024, 262144) == 1 << 30
+
+
+def _cache(n_rows=0, n_rem=0, cap=16, dim=128, dtype=1, ratio=4, rows=FAKE, rem=FAKE):
+    return dsv4_pool_cache(rows, rem, cap, n_rows, n_rem, ratio, dim, dtype)
+
+
+def _rc(name, *args):
+    return getattr(dsv4.lib(), name)(*args)
+
+
+def test_compress_validation_leaves_state():
+    c = _cache(n_rows=15, n_rem=3)
+    before = (c.n_rows, c.n_rem)
+    # 3 waiting + 5 new = 2 rows -> 17 > 16
+    assert _rc("dsv4_compress", ctypes.byref(c), ctypes.c_void_p(FAKE), 5, None) == CAPACITY
+    assert (c.n_rows, c.n_rem) == before
+    assert "capacity" in dsv4.dsv4_last_error()
+    assert _rc("dsv4_compress", ctypes.byref(c), None, 1, None) == INVALID
+    assert _rc("dsv4_compress", ctypes.byref(c), ctypes.c_void_p(FAKE), -1, None) == INVALID
+    bad = _cache(ratio=128)
+    assert _rc("dsv4_compress", ctypes.byref(bad), ctypes.c_void_p(FAKE), 4, None) == UNSUPPORTED
+    bad = _cache(n_rem=4)
+    assert _rc("dsv4_compress", ctypes.byref(bad), ctypes.c_void_p(FAKE), 4, None) == INVALID
+    assert _rc("dsv4_compress", None, ctypes.c_void_p(FAKE), 4, None) == INVALID
+    # nothing to do: no enqueue, OK
+    assert _rc("dsv4_compress", ctypes.byref(c), None, 0, None) == OK
+    assert (c.n_rows, c.n_rem) == before
+
+
+def test_select_guard_and_gates():
+    c = _cache(n_rows=10, n_rem=0, cap=64)
+    out = ctypes.c_void_p(FAKE)
+    ap = ctypes.c_int32(7)
+    args = lambda **kw: dict(dict(n_attn=10, q=FAKE, w=FAKE, T=8, q_pos0=32, heads=64, topk=4,
+                                  tile=0, scratch=FAKE, sbytes=1 << 20), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return _rc("dsv4_indexer_select", ctypes.byref(c), a["n_attn"], ctypes.c_void_p(a["q"]),
+                   ctypes.c_void_p(a["w"]), a["T"], a["q_pos0"], a["heads"], a["topk"], a["tile"],
+                   ctypes.c_void_p(a["scratch"]), a["sbytes"], out, ctypes.byref(ap), None)
+    assert call(n_attn=11) == MISMATCH            # row-count guard
+    assert "pooled rows" in dsv4.dsv4_last_error()
+    assert call(topk=0) == UNSUPPORTED
+    assert call(topk=5000) == UNSUPPORTED
+    assert call(q_pos0=40) == INVALID             # 40 + 8 > 4*10: ahead of the frontier
+    assert call(heads=65) == UNSUPPORTED
+    assert call(sbytes=10) == SCRATCH
+    assert call(q=0) == INVALID
+    assert ap.value == 7                          # untouched on every failure
+
+
+def test_scores_and_topk_gates():
+    c = _cache(n_rows=10, dim=96)
+    assert _rc("dsv4_indexer_scores", ctypes.byref(c), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+               4, 0, 64, 1, ctypes.c_void_p(FAKE), 64, None) == UNSUPPORTED
+    c = _cache(n_rows=10, dim=128, dtype=2)
+    assert _rc("dsv4_indexer_scores", ctypes.byref(c), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+               4, 0, 64, 1, ctypes.c_void_p(FAKE), 64, None) == UNSUPPORTED
+    c = _cache(n_rows=10, dim=128)
+    assert _rc("dsv4_indexer_scores", ctypes.byref(c), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+               4, 0, 64, 1, ctypes.c_void_p(FAKE), 8, None) == INVALID  # stride < rows
+    # top-k: visible prefix of the last row (position 99 -> 25 rows) exceeds 20 columns
+    assert _rc("dsv4_topk_select", ctypes.c_void_p(FAKE), 4, 64, 96, 20, 8,
+               ctypes.c_void_p(FAKE), None) == INVALID
+    assert _rc("dsv4_topk_select", ctypes.c_void_p(FAKE), 4, 64, 0, 20, 0,
+               ctypes.c_void_p(FAKE), None) == UNSUPPORTED
+
+
+def test_attention_gates():
+    c = _cache(n_rows=40, dim=512, cap=64)
+
+    def call(T=4, q_pos0=100, heads=64, dim=512, raw_pos0=0, n_raw=104, window=128, cache=c,
+             sel=FAKE, topk=16):
+        return _rc("dsv4_sparse_prefill_attn", ctypes.c_void_p(FAKE), T, q_pos0, heads, dim, 0.0,
+                   ctypes.c_void_p(FAKE), raw_pos0, n_raw, window, ctypes.byref(cache),
+                   ctypes.c_void_p(sel), topk, ctypes.c_void_p(FAKE), None)
+    assert call(dim=96) == UNSUPPORTED
+    assert call(dim=256) == INVALID           # cache dim differs
+    assert call(heads=65) == UNSUPPORTED
+    assert call(window=0) == INVALID
+    assert call(raw_pos0=1, n_raw=103) == INVALID   # window of position 100 starts at 0
+    assert call(n_raw=103) == INVALID          # does not reach position 103
+    assert call(q_pos0=200, raw_pos0=73, n_raw=131) == INVALID  # sees 51 pooled rows > 40
+    assert call(topk=0) == UNSUPPORTED
+    f32 = _cache(n_rows=40, dim=512, cap=64, dtype=2)
+    assert call(cache=f32) == UNSUPPORTED
