@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the DeepSeek-V4 indexed-attention prefill hot path on one MI355X.
+
+One step = one pass of the whole hot path over one prefill chunk of the
+workload: compress the chunk's raw KV rows into the attention PoolingCache,
+compress its raw index keys into the indexer PoolingCache, indexer score +
+top-k (dsv4_indexer_select), fused windowed + pooled attention.  Before each
+step the caches' host counters are reset to the prefix state, so every step
+appends the same rows at the same offsets.  Inputs are resident in HBM before
+the timed region.
+
+Prints one JSON line.  `value` is the headline metric, indexer score+top-k
+query rows per second (chunk rows / mean time of dsv4_indexer_select inside the
+timed steps, measured with HIP events on the launch stream).  `roofline` is
+for the dominant kernel, the MFMA indexer score, timed with HIP events over
+its own launches in the same configuration; `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload's query rows.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-seconds S]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import synthetic_inputs as SI
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=SI.CTX_128K.name, choices=sorted(SI.WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-time budget of the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+class Setup:
+    """Device state of one chunk of the workload (caches at the prefix state)."""
+
+    def __init__(self, wl: SI.Workload, seed: int):
+        import sparse_indexed_attention_amd as dsv4
+        self.dsv4 = dsv4
+        self.wl = wl
+        inp = SI.make_inputs(wl, seed)
+        if not wl.bf16:
+            for k in list(inp):
+                if isinstance(inp[k], np.ndarray) and k != "w":
+                    inp[k], inp[k + "_t"] = SI.as_bf16(inp[k])[1], SI.as_bf16(inp[k])[0]
+        self.inp = inp
+        self.n_prefix = wl.prefix_tokens // 4
+        self.icache = dsv4.PoolCache(wl.capacity_rows, wl.idx_dim)
+        self.acache = dsv4.PoolCache(wl.capacity_rows, wl.head_dim)
+        if self.n_prefix:
+            self.icache.rows[:self.n_prefix].copy_(inp["prefix_idx_rows_t"])
+            self.acache.rows[:self.n_prefix].copy_(inp["prefix_attn_rows_t"])
+        self.raw_pos0 = inp["raw_pos0"]
+        self.raw_kv = inp["raw_kv_t"].cuda()
+        self.chunk_kv = self.raw_kv[wl.q_pos0 - self.raw_pos0:]
+        self.idx_keys = inp["idx_keys_t"].cuda()
+        self.q_idx = inp["q_idx_t"].cuda()
+        self.w = inp["w_t"].cuda()
+        self.q_attn = inp["q_attn_t"].cuda()
+        T = wl.chunk
+        self.tile = wl.tile_rows if wl.tile_rows else T
+        self.S_after = wl.n_rows_after
+        self.scratch = torch.empty(dsv4.dsv4_indexer_scratch_bytes(self.tile, self.S_after) // 4,
+                                   device="cuda")
+        self.idx = torch.empty((T, wl.topk), dtype=torch.int32, device="cuda")
+        self.out = torch.empty((T, wl.heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+
+    def reset(self):
+        self.icache.set_state(self.n_prefix, 0)
+        self.acache.set_state(self.n_prefix, 0)
+
+    def step(self, ev=None):
+        d, wl = self.dsv4, self.wl
+        self.reset()
+        if ev: ev[0].record()
+        d.dsv4_compress(self.acache, self.chunk_kv)
+        d.dsv4_compress(self.icache, self.idx_keys)
+        if ev: ev[1].record()
+        ap = d.dsv4_indexer_select(self.icache, self.acache.n_rows, self.q_idx, self.w, wl.chunk,
+                                   wl.q_pos0, wl.idx_heads, wl.topk, self.idx, self.scratch,
+                                   wl.tile_rows)
+        if ev: ev[2].record()
+        d.dsv4_sparse_prefill_attn(self.q_attn, wl.q_pos0, self.raw_kv, self.raw_pos0, wl.window,
+                                   self.acache, self.idx, self.out)
+        if ev: ev[3].record()
+        return ap
+
+
+def timed_kernel(fn, reps: int) -> float:
+    """Mean ms per call of fn() measured with HIP events on the current stream."""
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def cpu_baseline(setup: Setup, budget_s: float):
+    """The CPU oracle (score + top-k) on a bounded sample of the chunk's query rows."""
+    from oracle import dsv4_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    wl, inp = setup.wl, setup.inp
+    S = setup.S_after
+    st = O.PoolingCacheState(wl.idx_dim, S)
+    st.rows[:setup.n_prefix] = inp["prefix_idx_rows"]
+    st.n_rows = setup.n_prefix
+    O.compress(st, inp["idx_keys"])
+    keys = st.rows[:S]
+    rng = np.random.default_rng(1)
+    order = rng.permutation(wl.chunk)
+    t0 = time.perf_counter()
+    n = 0
+    while n < len(order) and (n < 4 or time.perf_counter() - t0 < budget_s):
+        t = int(order[n])
+        sc = O.indexer_scores(inp["q_idx"][t:t + 1], inp["w"][t:t + 1], keys, wl.q_pos0 + t, S)
+        O.topk_select(sc, wl.q_pos0 + t, wl.topk)
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "query rows/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} random query rows of the chunk (score + top-k, numpy fp64), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the hot path runs on one MI355X and this build "
+              "has no multi-GPU path (see the sharding note in the design notes).", file=sys.stderr)
+        sys.exit(2)
+    wl = SI.WORKLOADS[args.workload]
+    torch.cuda.init()
+    setup = Setup(wl, args.seed)
+    d = setup.dsv4
+    T = wl.chunk
+    for _ in range(args.warmup):
+        setup.step()
+    torch.cuda.synchronize()
+
+    # ---- timed steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    all_pooled = False
+    for k in range(args.steps):
+        all_pooled = setup.step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1e3 * wall / args.steps
+    comp = np.mean([e[0].elapsed_time(e[1]) for e in evs])
+    sel = np.mean([e[1].elapsed_time(e[2]) for e in evs])
+    attn = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+
+    # ---- per-kernel times, same launch configuration as inside the step
+    pairs = wl.visible_pairs()
+    S = setup.S_after
+    tile = setup.tile
+    tile_pairs = sum((p + 1) // 4 for p in range(wl.q_pos0 + T - tile, wl.q_pos0 + T))
+    stride = d.dsv4_score_stride(S)
+    sc_view = setup.scratch[:tile * stride].view(tile, stride)
+    t_last0 = T - tile
+    q_t, w_t = setup.q_idx[t_last0:], setup.w[t_last0:]
+    ms_score = timed_kernel(lambda: d.dsv4_indexer_scores(setup.icache, q_t, w_t, wl.q_pos0 + t_last0,
+                                                          sc_view, True), max(5, args.steps))
+    ms_topk = timed_kernel(lambda: d.dsv4_topk_select(sc_view, wl.q_pos0 + t_last0, S, wl.topk,
+                                                      setup.idx[t_last0:]), max(5, args.steps))
+    flops_per_pair = 2 * wl.idx_heads * wl.idx_dim
+    score_tflops = tile_pairs * flops_per_pair / (ms_score * 1e-3) / 1e12
+    topk_bytes = tile_pairs * 4 + tile * wl.topk * 4
+    topk_gbs = topk_bytes / (ms_topk * 1e-3) / 1e9
+
+    attn_flops = sum(4 * wl.heads * wl.head_dim
+                     * (min(wl.window, p + 1) + min(wl.topk, (p + 1) // 4))
+                     for p in range(wl.q_pos0, wl.q_pos0 + T))
+    attn_tflops = attn_flops / (attn * 1e-3) / 1e12
+
+    cpu = cpu_baseline(setup, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    rec = {
+        "metric": "indexer score+top-k query rows/s and pooled-row scores/s at 128K ctx; MFMA util",
+        "value": T / (sel * 1e-3),
+        "unit": "query rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the pages' 4K-1M contexts)",
+        "config": {"workload": wl.name, "context_tokens": wl.q_pos0 + T, "chunk": T,
+                   "tile_rows": tile, "pooled_rows": S, "topk": wl.topk,
+                   "indexer_heads": wl.idx_heads, "indexer_dim": wl.idx_dim,
+                   "heads": wl.heads, "head_dim": wl.head_dim, "window": wl.window},
+        "pair_scores_per_s": pairs / (sel * 1e-3),
+        "step_query_rows_per_s": T / (ms_step * 1e-3),
+        "ms": {"compress_both": comp, "indexer_select": sel, "attention": attn,
+               "score_kernel": ms_score, "topk_kernel": ms_topk},
+        "all_pooled_path": bool(all_pooled),
+        "roofline": {"bound": "mfma", "kernel": "indexer_score", "achieved": score_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": score_tflops / PEAK_BF16_TFLOPS, "traffic": None},
+        "topk_roofline": {"bound": "hbm", "achieved": topk_gbs, "peak": PEAK_HBM_GBS,
+                          "unit": "GB/s", "frac": topk_gbs / PEAK_HBM_GBS},
+        "attn_roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
+                          "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()
