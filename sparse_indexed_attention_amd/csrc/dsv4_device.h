@@ -26,10 +26,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// Two floats -> packed bf16x2 (low half = a).
+// Two floats -> packed bf16x2 (low half = a), round to nearest even, using
+// gfx950's v_cvt_pk_bf16_f32 (what a __bf16 conversion lowers to).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16_bits(a)) |
-         (static_cast<uint32_t>(f32_to_bf16_bits(b)) << 16);
+  const bf16x2_t v = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// float -> bf16 bits with the hardware conversion (round to nearest even).
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // Order-preserving unsigned key of a float: a < b  <=>  key(a) < key(b) for

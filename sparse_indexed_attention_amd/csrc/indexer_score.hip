@@ -12,22 +12,28 @@
 // Mapping onto CDNA4.  This is a dense contraction (per query: a 64x128 by
 // 128xS product), so it runs on v_mfma_f32_32x32x16_bf16:
 //   * M = indexer heads (one or two 32-row tiles), K = index dim, N = pooled
-//     rows.  Each wave owns one query; its q block (heads x dim, bf16) stays
-//     in VGPRs for the whole sweep over its column range, as do its head
-//     weights.
-//   * Pooled index keys are staged through LDS in 64-row tiles shared by the
-//     8 waves (8 queries) of a workgroup; each key byte fetched from L2 feeds
-//     8 queries' MFMAs.  Rows are padded by 16 bytes so the 16-byte B-operand
-//     reads of 16 consecutive rows fall in distinct banks.
+//     rows.  Each wave owns two queries; their q blocks (heads x dim, bf16)
+//     stay in VGPRs for the whole sweep over the workgroup's column range, so
+//     every key fragment read from LDS feeds both queries' MFMAs.
+//   * Pooled index keys are gathered 64 rows at a time straight into LDS with
+//     global_load_lds_dwordx4 (no VGPRs hold data in flight), three LDS stages
+//     deep with one barrier per tile; 16-byte chunk c of row r sits at slot
+//     c ^ (r & 15), so the B-operand reads (32 rows, one chunk) are free of
+//     bank conflicts.
 //   * The contraction index is permuted identically in A and B: lane half kb
 //     holds dims [kb*D/2, kb*D/2 + D/2), so every lane reads one contiguous
-//     run of D bytes from its q row and its key row.
+//     run of D bytes from its q rows.
 //   * Epilogue in the accumulator layout: each lane holds 16 head rows of one
 //     column per M tile; ReLU and the weight are one max + one fma per
-//     element, the lane sums its rows, and one v_permlane32_swap adds the
-//     other lane half.  The mask compares the column with the query's visible
-//     count; fully masked column tiles are written as -inf without MFMA work.
-//   * Grid: the workgroups are dealt round-robin to the 8 XCDs; a workgroup's
+//     element (weights read from LDS), the lane sums its rows, and one
+//     v_permlane32_swap both finishes the head sum and leaves query 0's
+//     column in lanes 0-31 and query 1's in lanes 32-63 for a single store.
+//     The mask compares the column with the query's visible count; column
+//     blocks no query of the wave can see are written as -inf without MFMA
+//     work.
+//   * Four-wave workgroups, two per CU: their barriers are independent, so one
+//     workgroup's epilogue VALU work overlaps the other's MFMAs.
+//   * Grid: workgroups are dealt round-robin to the 8 XCDs; a workgroup's
 //     column split is chosen from blockIdx % 8 so each XCD sweeps one eighth
 //     of the key rows, which then stays resident in that XCD's L2.
 #include "dsv4_device.h"
@@ -36,20 +42,40 @@ using namespace dsv4;
 
 namespace {
 
-constexpr int kWaves = 8;     // queries per workgroup (one per wave)
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kTileCols = 64; // key rows per LDS tile
+constexpr int kQW = 2;                 // queries per wave
+constexpr int kQB = kWaves * kQW;      // queries per workgroup
+constexpr int kTileCols = 64;          // key rows per LDS tile
+constexpr int kStages = 3;
+
+__device__ __forceinline__ void global_to_lds16(const void* g, const void* lds_wave_base) {
+  // 16 bytes per lane from global memory straight into LDS (lane L writes
+  // lds_wave_base + 16*L).  Inline asm: the compiler neither reorders it nor
+  // adds its own conservative waits; the kernel waits with s_waitcnt vmcnt.
+  const uint32_t lds = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_wave_base));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
 
 template <int KSTEPS, int MT>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, 2)
 indexer_score_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
                      const uint16_t* __restrict__ keys, int64_t rows, int64_t q_pos0, int64_t S,
                      int n_heads, int fold_mask, float* __restrict__ out, int64_t out_stride,
                      int splits_per_xcd, int64_t cols_per_split) {
   constexpr int D = KSTEPS * 16;
-  constexpr int PITCH = D + 8;               // uint16 per LDS row (16 B pad)
-  constexpr int CHUNKS = kTileCols * D / 8;  // 16-byte chunks per tile
-  __shared__ __attribute__((aligned(16))) uint16_t ktile[kTileCols * PITCH];
+  constexpr int CPR = D / 8;                 // 16-byte chunks per key row
+  constexpr int SWZ = CPR >= 16 ? 15 : CPR - 1;
+  constexpr int RPI = 64 / CPR;              // key rows per DMA instruction
+  constexpr int INSTS = kTileCols / RPI;     // DMA instructions per tile
+  constexpr int PER_WAVE = INSTS / kWaves;   // ... per wave
+  static_assert(INSTS % kWaves == 0 && PER_WAVE >= 1 && PER_WAVE <= 15, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint16_t ktile[kStages][kTileCols * D];
+  __shared__ __attribute__((aligned(16))) float w_lds[kQB][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -67,125 +93,132 @@ indexer_score_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w
   if (col_end > S) col_end = S;
   if (col_begin >= col_end) return;  // whole workgroup: no barrier reached yet
 
-  const int64_t t = qb * kWaves + wave;
-  const bool tvalid = t < rows;
-  int64_t t_last = qb * kWaves + (kWaves - 1);
+  const int64_t t0 = qb * kQB + wave * kQW;  // this wave's queries t0, t0+1
+  int64_t vis[kQW];
+  bool tval[kQW];
+#pragma unroll
+  for (int qi = 0; qi < kQW; ++qi) {
+    tval[qi] = t0 + qi < rows;
+    int64_t v = S;
+    if (fold_mask) {
+      v = tval[qi] ? visible_rows(q_pos0 + t0 + qi) : 0;
+      if (v > S) v = S;
+    }
+    vis[qi] = tval[qi] ? v : 0;
+  }
+  const int64_t vis_wave = vis[0] > vis[1] ? vis[0] : vis[1];
+  int64_t t_last = qb * kQB + (kQB - 1);
   if (t_last > rows - 1) t_last = rows - 1;
-  int64_t vis_t = S, vis_max = S;
+  int64_t vis_max = S;
   if (fold_mask) {
-    vis_t = tvalid ? visible_rows(q_pos0 + t) : 0;
-    if (vis_t > S) vis_t = S;
     vis_max = visible_rows(q_pos0 + t_last);
     if (vis_max > S) vis_max = S;
   }
   int64_t compute_end = col_end < vis_max ? col_end : vis_max;
   if (compute_end < col_begin) compute_end = col_begin;
 
-  // ---- per-wave operands held in registers for the whole sweep
-  bf16x8_t afrag[MT][KSTEPS];
-  float wv[MT][16];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int head = mt * 32 + ln;
-    const bool hv = tvalid && head < n_heads;
-    const uint16_t* qp = q + ((t * n_heads + head) * (int64_t)D + kb * (D / 2));
-#pragma unroll
-    for (int j = 0; j < KSTEPS; ++j) {
-      if (hv) {
-        afrag[mt][j] = *reinterpret_cast<const bf16x8_t*>(qp + j * 8);
-      } else {
-        afrag[mt][j] = bf16x8_t{};
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int hh = mt * 32 + 8 * (i >> 2) + 4 * kb + (i & 3);
-      wv[mt][i] = (tvalid && hh < n_heads) ? w[t * n_heads + hh] : 0.f;
-    }
+  // ---- head weights of the workgroup's queries -> LDS (0 for missing heads)
+  for (int i = tid; i < kQB * 64; i += kThreads) {
+    const int ql = i >> 6, h = i & 63;
+    const int64_t tq = qb * kQB + ql;
+    w_lds[ql][h] = (tq < rows && h < n_heads) ? w[tq * n_heads + h] : 0.f;
   }
 
-  // ---- sweep column tiles that some query of this workgroup can see
+  // ---- the wave's q blocks, held in registers for the whole sweep
+  bf16x8_t afrag[kQW][MT][KSTEPS];
+#pragma unroll
+  for (int qi = 0; qi < kQW; ++qi)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int head = mt * 32 + ln;
+      const bool hv = tval[qi] && head < n_heads;
+      const uint16_t* qp = q + (((t0 + qi) * n_heads + head) * (int64_t)D + kb * (D / 2));
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j)
+        afrag[qi][mt][j] = hv ? *reinterpret_cast<const bf16x8_t*>(qp + j * 8) : bf16x8_t{};
+    }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): only tile DMAs in flight from here
+
   const int64_t n_tiles = (compute_end - col_begin + kTileCols - 1) / kTileCols;
-  constexpr int PER_THREAD = (CHUNKS + kThreads - 1) / kThreads;
-  u32x4_t pre[PER_THREAD];
-
-  auto load_tile = [&](int64_t c0) {
-#pragma unroll
-    for (int k = 0; k < PER_THREAD; ++k) {
-      const int ci = tid + k * kThreads;
-      pre[k] = u32x4_t{0u, 0u, 0u, 0u};
-      if (ci < CHUNKS) {
-        const int rr = ci / (D / 8);
-        const int c8 = ci - rr * (D / 8);
-        const int64_t col = c0 + rr;
-        if (col < compute_end)
-          pre[k] = *reinterpret_cast<const u32x4_t*>(keys + col * D + c8 * 8);
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int k = 0; k < PER_THREAD; ++k) {
-      const int ci = tid + k * kThreads;
-      if (ci < CHUNKS) {
-        const int rr = ci / (D / 8);
-        const int c8 = ci - rr * (D / 8);
-        *reinterpret_cast<u32x4_t*>(&ktile[rr * PITCH + c8 * 8]) = pre[k];
-      }
-    }
-  };
-
-  if (n_tiles > 0) {
-    load_tile(col_begin);
-    store_tile();
-  }
-  __syncthreads();
-
-  float* orow = out + t * out_stride;
-  for (int64_t it = 0; it < n_tiles; ++it) {
+  auto issue_tile = [&](int64_t it, int buf) {
     const int64_t c0 = col_begin + it * kTileCols;
-    if (it + 1 < n_tiles) load_tile(c0 + kTileCols);  // in flight during MFMA work
+#pragma unroll
+    for (int k = 0; k < PER_WAVE; ++k) {
+      const int inst = wave * PER_WAVE + k;
+      const int row = inst * RPI + lane / CPR;
+      const int slot = lane % CPR;
+      int64_t col = c0 + row;
+      if (col >= compute_end) col = col_begin;  // any valid row; never stored
+      global_to_lds16(keys + col * D + (slot ^ (row & SWZ)) * 8, &ktile[buf][inst * RPI * D]);
+    }
+  };
 
-    if (tvalid) {
+  if (n_tiles > 0) issue_tile(0, 0);
+  if (n_tiles > 1) issue_tile(1, 1);
+
+  float* orow = out + (t0 + kb) * out_stride;
+  const bool lane_tval = kb == 0 ? tval[0] : tval[1];
+  const int64_t lane_vis = kb == 0 ? vis[0] : vis[1];
+
+  for (int64_t it = 0; it < n_tiles; ++it) {
+    const int buf = static_cast<int>(it % kStages);
+    if (it + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0F70 | PER_WAVE);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();  // publishes tile `it`, retires tile it-1 (its stage takes it+2)
+    if (it + 2 < n_tiles) issue_tile(it + 2, static_cast<int>((it + 2) % kStages));
+    const int64_t c0 = col_begin + it * kTileCols;
+    const uint16_t* tb = ktile[buf];
 #pragma unroll
-      for (int sub = 0; sub < kTileCols / 32; ++sub) {
-        const int64_t s0 = c0 + sub * 32;
-        const int64_t col = s0 + ln;
-        if (s0 >= col_end) break;
-        if (s0 >= vis_t) {  // whole 32-column block masked for this query
-          if (kb == 0 && col < col_end) orow[col] = -INFINITY;
-          continue;
-        }
-        bf16x8_t bfrag[KSTEPS];
-        const uint16_t* kp = &ktile[(sub * 32 + ln) * PITCH + kb * (D / 2)];
+    for (int sub = 0; sub < kTileCols / 32; ++sub) {
+      const int64_t s0 = c0 + sub * 32;
+      if (s0 >= col_end) break;
+      const int64_t col = s0 + ln;
+      if (s0 >= vis_wave) {  // neither query of the wave sees this block
+        if (lane_tval && col < col_end) orow[col] = -INFINITY;
+        continue;
+      }
+      const int row = sub * 32 + ln;
+      bf16x8_t bfrag[KSTEPS];
 #pragma unroll
-        for (int j = 0; j < KSTEPS; ++j) bfrag[j] = *reinterpret_cast<const bf16x8_t*>(kp + j * 8);
-        float part = 0.f;
+      for (int j = 0; j < KSTEPS; ++j) {
+        const int chunk = kb * KSTEPS + j;
+        bfrag[j] = *reinterpret_cast<const bf16x8_t*>(tb + row * D + ((chunk ^ (row & SWZ)) * 8));
+      }
+      float part[kQW];
+#pragma unroll
+      for (int qi = 0; qi < kQW; ++qi) {
+        part[qi] = 0.f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           f32x16_t acc = {};
 #pragma unroll
           for (int j = 0; j < KSTEPS; ++j)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[mt][j], bfrag[j], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[qi][mt][j], bfrag[j], acc, 0, 0, 0);
+          // accumulator element i holds head mt*32 + 8*(i/4) + 4*kb + i%4
+          const float* wp = &w_lds[wave * kQW + qi][mt * 32 + 4 * kb];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) part = fmaf(wv[mt][i], fmaxf(acc[i], 0.f), part);
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(wp + 8 * g4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              part[qi] = fmaf(wv[i], fmaxf(acc[4 * g4 + i], 0.f), part[qi]);
+          }
         }
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
-                                                         __float_as_uint(part), false, false);
-        const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        if (kb == 0 && col < col_end) orow[col] = (col < vis_t) ? tot : -INFINITY;
       }
-    }
-    __syncthreads();
-    if (it + 1 < n_tiles) {
-      store_tile();
-      __syncthreads();
+      // lanes 0-31 <- query 0 (both halves summed), lanes 32-63 <- query 1
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
+                                                       __float_as_uint(part[1]), false, false);
+      const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      if (lane_tval && col < col_end) orow[col] = (col < lane_vis) ? tot : -INFINITY;
     }
   }
 
   // ---- columns no query of this workgroup can see: sentinel only
-  if (tvalid) {
-    for (int64_t col = compute_end + lane; col < col_end; col += 64) orow[col] = -INFINITY;
+#pragma unroll
+  for (int qi = 0; qi < kQW; ++qi) {
+    if (!tval[qi]) continue;
+    float* orq = out + (t0 + qi) * out_stride;
+    for (int64_t col = compute_end + lane; col < col_end; col += 64) orq[col] = -INFINITY;
   }
 }
 
@@ -193,10 +226,10 @@ template <int KSTEPS, int MT>
 hipError_t launch_t(const void* q, const float* w, const void* keys, int64_t rows,
                     int64_t q_pos0, int64_t S, int n_heads, int fold_mask, float* out,
                     int64_t out_stride, hipStream_t s) {
-  const int64_t nqb = (rows + kWaves - 1) / kWaves;
+  const int64_t nqb = (rows + kQB - 1) / kQB;
   // Column splits: a multiple of 8 (one group per XCD), enough workgroups to
-  // fill 256 CUs several times, and at least one 64-column tile per split.
-  int64_t per_xcd = (2048 + 8 * nqb - 1) / (8 * nqb);
+  // fill 256 CUs several times, and at least one tile per split.
+  int64_t per_xcd = (4096 + 8 * nqb - 1) / (8 * nqb);
   int64_t max_per_xcd = S / (8 * kTileCols);
   if (max_per_xcd < 1) max_per_xcd = 1;
   if (per_xcd > max_per_xcd) per_xcd = max_per_xcd;

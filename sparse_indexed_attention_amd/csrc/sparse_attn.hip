@@ -13,49 +13,93 @@
 // shared by all heads); out = softmax(scale * q.K) . K.
 //
 // Mapping onto CDNA4:
-//   * one workgroup per query, one wave per 16 heads (4 waves at H = 64);
-//   * keys are gathered 32 at a time (each row contiguous, 16-byte loads,
-//     one 1 KiB row per 64 lanes) into LDS twice: row-major for the QK^T
-//     operand and transposed (dims x keys) for the PV operand;
+//   * one workgroup per query; a wave owns 16 heads and one half of the head
+//     dimension (8 waves at H = 64, D = 512), so its Q block (B operand) and
+//     its O block (16 heads x D/2, fp32) stay in registers with room left for
+//     two waves per SIMD, which hide each other's LDS latency;
+//   * keys are gathered 32 at a time straight into LDS with
+//     global_load_lds_dwordx4 (each wave instruction moves 64 x 16 B, one whole
+//     1 KiB row at D = 512), three LDS stages deep: the gathers of tiles i+1
+//     and i+2 are in flight while tile i is computed, and no VGPRs hold
+//     in-flight data;
+//   * 16-byte chunk c of row r sits at slot c ^ (r & 15), which keeps both LDS
+//     read patterns below free of bank conflicts;
 //   * QK^T is computed transposed, S^T = K . Q^T, with
-//     v_mfma_f32_16x16x32_bf16: the wave's Q block is the B operand and
-//     stays in VGPRs; in the result each lane holds 8 keys of one head, which
-//     is exactly the A-operand layout PV needs (the key order inside the
+//     v_mfma_f32_16x16x32_bf16, each wave over its half of the dims; the two
+//     halves' partial tiles are summed through LDS (a + b == b + a, so both
+//     waves hold bit-identical scores).  In S^T each lane holds 8 keys of one
+//     head, exactly the A-operand layout PV needs (key order inside the
 //     contraction is permuted the same way for P and V), so probabilities
 //     never leave the lane;
-//   * online softmax in fp32 (exp2 with the scale folded in), running max
-//     and sum per head reduced across the four 16-lane groups;
-//   * O (16 heads x D per wave) accumulates in fp32 registers; the final
-//     1/sum scaling and bf16 rounding happen once at the end.
+//   * PV reads its B operand (4 keys x 16 dims per 16-lane block) from the same
+//     row-major tile with ds_read_b64_tr_b16, which transposes in the LDS read
+//     path; no second, transposed copy of the tile is written;
+//   * online softmax in fp32 (exp2, scale folded in) against a lazily moved
+//     reference max: O is rescaled only on tiles where some head's max passes
+//     the reference by more than 2^8, keeping p <= 256 (exact math, rounding
+//     of p to bf16 is scale-free);
+//   * O is normalised, rounded to bf16 and staged through LDS once at the end
+//     for 16-byte coalesced stores.
+// Masked key slots (empty, invisible or past the end) are loaded from the
+// query's own raw row so the tile never holds non-finite data, and their
+// logits are set to -inf.
 #include "dsv4_device.h"
 
 using namespace dsv4;
 
 namespace {
 
-constexpr int kKeys = 32;  // keys per LDS tile
+constexpr int kKeys = 32;   // keys per LDS tile
+constexpr int kStages = 3;  // LDS tile stages: two tiles in flight while one is computed
 
-template <int D, int NW>
-__global__ void __launch_bounds__(NW * 64)
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// 16 bytes per lane from global memory straight into LDS: lane L of the wave
+// writes lds_wave_base + 16*L.  Issued as inline asm so the compiler neither
+// reorders it nor adds its own (conservative, vmcnt(0)) waits for it: the
+// kernel waits for these loads itself with s_waitcnt vmcnt before the barrier
+// that publishes a tile.  Being issued after the compiler's own loads, they
+// can only make the compiler's in-order vmcnt waits stricter, never weaker.
+__device__ __forceinline__ void global_to_lds16(const void* g, const void* lds_wave_base) {
+  const uint32_t lds = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_wave_base));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
+template <int D, int NHG, int DSPLIT>
+__global__ void __launch_bounds__(NHG * DSPLIT * 64)
 sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float scale_log2,
                    const uint16_t* __restrict__ raw, int64_t raw_pos0, int window,
                    const uint16_t* __restrict__ pooled, const int32_t* __restrict__ sel,
                    int topk, uint16_t* __restrict__ out) {
+  constexpr int NW = NHG * DSPLIT;
   constexpr int NT = NW * 64;
-  constexpr int KP = D + 8;        // row-major key tile pitch (uint16)
-  constexpr int VP = kKeys + 8;    // transposed tile pitch (uint16)
-  constexpr int KSTEP = D / 32;    // QK^T contraction steps
-  constexpr int NTILE = D / 16;    // PV output column tiles
-  constexpr int CPR = D / 8;       // 16-byte chunks per row
-  __shared__ __attribute__((aligned(16))) uint16_t ktile[kKeys * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t vtile[D * VP];
-  __shared__ int s_valid[kKeys];
+  constexpr int DH = D / DSPLIT;          // dims per wave
+  constexpr int CPR = D / 8;              // 16-byte chunks per row
+  constexpr int SWZ = CPR >= 16 ? 15 : CPR - 1;
+  constexpr int RPI = 64 / CPR;           // rows per 64-lane load instruction
+  constexpr int INSTS = kKeys / RPI;      // load instructions per tile
+  constexpr int KSTEP = DH / 32;          // QK^T contraction steps per wave
+  constexpr int NTILE = DH / 16;          // PV output column tiles per wave
+  constexpr int TILE_ELEMS = kKeys * D;
+  static_assert(RPI >= 1 && kKeys % RPI == 0 && KSTEP >= 1, "tile shape");
+  // load instructions every wave issues per tile (waves may issue one more)
+  constexpr int kNewer = INSTS / NW < 15 ? INSTS / NW : 15;
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[kStages][TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) float xs[DSPLIT > 1 ? NW : 1][DSPLIT > 1 ? 64 * 8 : 1];
   __shared__ int s_last;
+  extern __shared__ int s_sel[];  // the query's selection row (topk ints, dynamic)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int kb = lane >> 4;   // 16-lane group
+  const int hg = wave % NHG;   // head group
+  const int dh = wave / NHG;   // dim half
+  const int kb = lane >> 4;    // 16-lane group
   const int l16 = lane & 15;
 
   const int64_t t = blockIdx.x;
@@ -63,8 +107,9 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
   const int64_t lo = (p - window + 1) > 0 ? (p - window + 1) : 0;
   const int n_win = static_cast<int>(p - lo + 1);
   const int64_t vis = visible_rows(p);
+  const uint16_t* self_row = raw + (p - raw_pos0) * D;  // always valid
 
-  // ---- number of pooled slots to walk
+  // ---- selection row into LDS; number of pooled slots to walk
   int n_slots;
   if (sel) {
     if (tid == 0) s_last = -1;
@@ -73,6 +118,7 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
     const int32_t* sp = sel + t * topk;
     for (int j = tid; j < topk; j += NT) {
       const int32_t s = sp[j];
+      s_sel[j] = s;
       if (s >= 0 && s < vis) last = j;
     }
     for (int off = 32; off > 0; off >>= 1) last = max(last, __shfl_xor(last, off));
@@ -85,79 +131,147 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
   const int n_keys = n_win + n_slots;
   const int n_tiles = (n_keys + kKeys - 1) / kKeys;
 
-  // ---- this wave's Q block (B operand of S^T = K.Q^T)
-  const int head = wave * 16 + l16;
+  auto key_row = [&](int j) -> const uint16_t* {  // row of key slot j, or nullptr
+    if (j < n_win) return raw + (lo + j - raw_pos0) * D;
+    if (j < n_keys) {
+      const int sl = j - n_win;
+      const int64_t s = sel ? static_cast<int64_t>(s_sel[sl]) : sl;
+      if (s >= 0 && s < vis) return pooled + s * D;
+    }
+    return nullptr;
+  };
+
+  // Gather tile `tile` into stage `buf`: instruction i moves rows
+  // i*RPI .. i*RPI+RPI-1, lane -> (row, slot).
+  auto issue_tile = [&](int tile, int buf) {
+    for (int i = wave; i < INSTS; i += NW) {
+      const int row = i * RPI + lane / CPR;
+      const int slot = lane % CPR;
+      const uint16_t* rp = key_row(tile * kKeys + row);
+      if (!rp) rp = self_row;
+      global_to_lds16(rp + (slot ^ (row & SWZ)) * 8, &tiles[buf][i * RPI * D]);
+    }
+  };
+
+  // ---- Q block (B operand of S^T = K.Q^T): lane group kb holds dims
+  // dh*DH + kb*DH/4 .. + DH/4 over the KSTEP steps
+  const int head = hg * 16 + l16;
   const bool hv = head < H;
   bf16x8_t qf[KSTEP];
   {
-    const uint16_t* qp = q + ((t * H + head) * (int64_t)D + kb * (D / 4));
+    const uint16_t* qp = q + ((t * H + head) * (int64_t)D + dh * DH + kb * (DH / 4));
 #pragma unroll
     for (int j = 0; j < KSTEP; ++j)
       qf[j] = hv ? *reinterpret_cast<const bf16x8_t*>(qp + j * 8) : bf16x8_t{};
   }
+  // Drain the compiler's own loads (Q) before the first LDS DMA is issued, so
+  // the only vector-memory operations in flight inside the loop are the tile
+  // gathers the loop accounts for.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   f32x4_t o[NTILE];
 #pragma unroll
   for (int n = 0; n < NTILE; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // per head (this lane's head l16)
+  float m_ref = -INFINITY;  // per head (this lane's head l16): reference max, log2 units
   float l_run = 0.f;
+  constexpr float kSlack = 8.f;
 
+  // key order inside a tile: M tile mt, row m -> key mt*16 + 4*(m%4) + m/4
+  // (so the 4 keys one tr16 read covers are rows kb, kb+4, kb+8, kb+12)
+  const int qk_row0 = 4 * (l16 & 3) + (l16 >> 2);
+  const int qk_row1 = 16 + qk_row0;
+  const int trow0 = 4 * (l16 >> 2) + kb;  // PV keys, mt = 0: 4*q + kb
+  const int trow1 = 16 + trow0;           // mt = 1
+  const int dsub = 4 * (l16 & 3);
+
+  issue_tile(0, 0);
+  if (n_tiles > 1) issue_tile(1, 1);
   for (int tile = 0; tile < n_tiles; ++tile) {
-    __syncthreads();  // previous tile fully consumed
-    // ---- gather 32 keys into LDS (row-major and transposed)
-    for (int ci = tid; ci < kKeys * CPR; ci += NT) {
-      const int kk = ci / CPR;
-      const int c8 = ci - kk * CPR;
-      const int j = tile * kKeys + kk;
-      const uint16_t* rp = nullptr;
-      if (j < n_win) {
-        rp = raw + (lo + j - raw_pos0) * D;
-      } else if (j < n_keys) {
-        const int slot = j - n_win;
-        int64_t s = sel ? static_cast<int64_t>(sel[t * topk + slot]) : slot;
-        if (s >= 0 && s < vis) rp = pooled + s * D;
-      }
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (rp) v = *reinterpret_cast<const u32x4_t*>(rp + c8 * 8);
-      if (c8 == 0) s_valid[kk] = rp != nullptr;
-      *reinterpret_cast<u32x4_t*>(&ktile[kk * KP + c8 * 8]) = v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vtile[(c8 * 8 + 2 * e) * VP + kk] = static_cast<uint16_t>(v[e] & 0xffffu);
-        vtile[(c8 * 8 + 2 * e + 1) * VP + kk] = static_cast<uint16_t>(v[e] >> 16);
-      }
-    }
+    const int buf = tile % kStages;
+    // wait for this wave's loads of `tile`; the loads of tile+1 (issued later,
+    // at least kNewer instructions per wave) may stay in flight
+    if (tile + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0F70 | kNewer);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // publishes `tile` and retires tile-1: its stage takes tile+2
     __syncthreads();
+    if (tile + 2 < n_tiles) issue_tile(tile + 2, (tile + 2) % kStages);
+    const uint16_t* tb = tiles[buf];
 
-    // ---- S^T (32 keys x 16 heads) = K . Q^T
-    f32x4_t sacc[2];
+    // ---- validity of the tile's 32 key slots as a wave-uniform bit mask
+    const uint32_t vmask = static_cast<uint32_t>(
+        __ballot(lane < kKeys && key_row(tile * kKeys + lane) != nullptr));
+
+    // ---- partial S^T (32 keys x 16 heads) over this wave's dims.  Fragment
+    // reads go out in batches; scheduling barriers keep batch b+1's reads
+    // issued ahead of batch b's MFMAs so LDS latency is paid once per batch.
+    f32x4_t sacc0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, sacc1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    {
+      constexpr int QB = KSTEP < 4 ? KSTEP : 4;  // k-steps per batch
+      const uint16_t* rb0 = tb + qk_row0 * D;
+      const uint16_t* rb1 = tb + qk_row1 * D;
+      bf16x8_t fa[2][2][QB];  // [buffer][m tile][step]
+      auto load_batch = [&](int j0, int bi) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      sacc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kp = &ktile[(mt * 16 + l16) * KP + kb * (D / 4)];
+        for (int u = 0; u < QB; ++u) {
+          const int chunk = dh * (DH / 8) + kb * KSTEP + j0 + u;
+          fa[bi][0][u] = *reinterpret_cast<const bf16x8_t*>(rb0 + ((chunk ^ (qk_row0 & SWZ)) * 8));
+          fa[bi][1][u] = *reinterpret_cast<const bf16x8_t*>(rb1 + ((chunk ^ (qk_row1 & SWZ)) * 8));
+        }
+      };
+      load_batch(0, 0);
 #pragma unroll
-      for (int j = 0; j < KSTEP; ++j) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kp + j * 8);
-        sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[j], sacc[mt], 0, 0, 0);
+      for (int j0 = 0; j0 < KSTEP; j0 += QB) {
+        const int bi = (j0 / QB) & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        if (j0 + QB < KSTEP) load_batch(j0 + QB, bi ^ 1);
+#pragma unroll
+        for (int u = 0; u < QB; ++u) {
+          sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[bi][0][u], qf[j0 + u], sacc0, 0, 0, 0);
+          sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[bi][1][u], qf[j0 + u], sacc1, 0, 0, 0);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // lane holds keys mt*16 + 4*kb + i (i < 4) for head l16
+    if constexpr (DSPLIT > 1) {
+      // sum with the partner wave (same heads, other dims)
+      *reinterpret_cast<f32x4_t*>(&xs[wave][lane * 8]) = sacc0;
+      *reinterpret_cast<f32x4_t*>(&xs[wave][lane * 8 + 4]) = sacc1;
+      __syncthreads();
+      const int partner = (wave + NHG) % NW;
+      sacc0 += *reinterpret_cast<const f32x4_t*>(&xs[partner][lane * 8]);
+      sacc1 += *reinterpret_cast<const f32x4_t*>(&xs[partner][lane * 8 + 4]);
+    }
+
+    // lane holds, for head l16, keys mt*16 + 4*i + kb (output rows 4*kb + i)
     float sv[8];
     float mx = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = mt * 16 + 4 * kb + i;
-        const float x = s_valid[kk] ? sacc[mt][i] * scale_log2 : -INFINITY;
-        sv[mt * 4 + i] = x;
-        mx = fmaxf(mx, x);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int k0 = 4 * i + kb, k1 = 16 + 4 * i + kb;
+      sv[i] = ((vmask >> k0) & 1u) ? sacc0[i] * scale_log2 : -INFINITY;
+      sv[4 + i] = ((vmask >> k1) & 1u) ? sacc1[i] * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, fmaxf(sv[i], sv[4 + i]));
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    // Lazy rescale: exponentials are taken against a reference max m_ref that
+    // only moves when the running max passes it by more than kSlack (log2
+    // units); p <= 2^kSlack stays far from fp32 / bf16 overflow.
+    const bool bump = mx > m_ref + kSlack;
+    if (__ballot(bump)) {
+      const float m_new = bump ? mx : m_ref;
+      const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
+      l_run *= alpha;
+      m_ref = m_new;
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kb + i);
+#pragma unroll
+      for (int n = 0; n < NTILE; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[n][i] *= al[i];
+    }
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
     float psum = 0.f;
     float pr[8];
 #pragma unroll
@@ -167,19 +281,11 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
     }
     psum += __shfl_xor(psum, 16);
     psum += __shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    l_run += psum;
 
-    // ---- rescale O rows (heads 4*kb + i) by their head's alpha
-    float al[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kb + i);
-#pragma unroll
-    for (int n = 0; n < NTILE; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[n][i] *= al[i];
-
-    // ---- P (A operand: head l16, keys {4kb+i, 16+4kb+i}) . V
+    // ---- O += P . V over this wave's dims; P = A operand (head l16, keys
+    // mt*16 + 4*i + kb); V via tr16: lane j of a 16-lane block addresses key
+    // q = j/4 of the 4 and dims 4*(j%4) .. +3 of the 16-dim column tile
     bf16x8_t pa;
     {
       uint32_t pk[4];
@@ -189,51 +295,90 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
       pk[3] = pack_bf16x2(pr[6], pr[7]);
       pa = *reinterpret_cast<const bf16x8_t*>(pk);
     }
+    {
+      constexpr int PB = NTILE < 4 ? NTILE : 4;  // column tiles per batch
+      const uint16_t* r0 = tb + trow0 * D;
+      const uint16_t* r1 = tb + trow1 * D;
+      const int sw0 = trow0 & SWZ, sw1 = trow1 & SWZ;
+      i16x4_t fv[2][2][PB];  // [buffer][key group][column tile]
+      auto load_batch = [&](int n0, int bi) {
 #pragma unroll
-    for (int n = 0; n < NTILE; ++n) {
-      const uint16_t* vp = &vtile[(n * 16 + l16) * VP];
-      uint32_t bk[4];
-      const uint2 lo4 = *reinterpret_cast<const uint2*>(vp + 4 * kb);
-      const uint2 hi4 = *reinterpret_cast<const uint2*>(vp + 16 + 4 * kb);
-      bk[0] = lo4.x; bk[1] = lo4.y; bk[2] = hi4.x; bk[3] = hi4.y;
-      const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(bk);
-      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, b, o[n], 0, 0, 0);
+        for (int u = 0; u < PB; ++u) {
+          const int d = dh * DH + (n0 + u) * 16 + dsub;
+          const int ch = d >> 3;
+          const int off = d & 7;
+          fv[bi][0][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(r0 + ((ch ^ sw0) * 8) + off));
+          fv[bi][1][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(r1 + ((ch ^ sw1) * 8) + off));
+        }
+      };
+      load_batch(0, 0);
+#pragma unroll
+      for (int n0 = 0; n0 < NTILE; n0 += PB) {
+        const int bi = (n0 / PB) & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        if (n0 + PB < NTILE) load_batch(n0 + PB, bi ^ 1);
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+          bf16x8_t b;
+          *reinterpret_cast<i16x4_t*>(&b) = fv[bi][0][u];
+          *(reinterpret_cast<i16x4_t*>(&b) + 1) = fv[bi][1][u];
+          o[n0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, b, o[n0 + u], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  __syncthreads();  // every wave is done with the tile stages
 
-  // ---- normalise and store: lane holds heads 4*kb + i, dim n*16 + l16
+  // ---- normalise, round, stage through LDS, store 16-byte chunks
   const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
   float iv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) iv[i] = __shfl(inv, 4 * kb + i);
+  static_assert(NW * 16 * DH <= kStages * TILE_ELEMS, "output staging fits the tile stages");
+  uint16_t* stage = &tiles[0][0] + wave * 16 * DH;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int hh = wave * 16 + 4 * kb + i;
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int n = 0; n < NTILE; ++n)
+      stage[(4 * kb + i) * DH + n * 16 + l16] = bf16_rne(o[n][i] * iv[i]);
+  constexpr int CPH = DH / 8;  // 16-byte chunks per head row of this wave
+  for (int c = lane; c < 16 * CPH; c += 64) {
+    const int hr = c / CPH;
+    const int hh = hg * 16 + hr;
     if (hh < H) {
-      uint16_t* op = out + (t * H + hh) * (int64_t)D;
-#pragma unroll
-      for (int n = 0; n < NTILE; ++n) op[n * 16 + l16] = f32_to_bf16_bits(o[n][i] * iv[i]);
+      *reinterpret_cast<u32x4_t*>(out + (t * H + hh) * (int64_t)D + dh * DH + (c % CPH) * 8) =
+          *reinterpret_cast<const u32x4_t*>(stage + hr * DH + (c % CPH) * 8);
     }
   }
 }
 
+template <int D, int NHG>
+hipError_t launch_hg(const dim3& grid, size_t dyn, hipStream_t s, const uint16_t* q, int64_t q_pos0,
+                     int H, float sl2, const uint16_t* raw, int64_t raw_pos0, int window,
+                     const uint16_t* pooled, const int32_t* sel, int topk, uint16_t* out) {
+  constexpr int DSPLIT = D >= 64 ? 2 : 1;
+  hipLaunchKernelGGL((sparse_attn_kernel<D, NHG, DSPLIT>), grid, dim3(NHG * DSPLIT * 64), dyn, s,
+                     q, q_pos0, H, sl2, raw, raw_pos0, window, pooled, sel, topk, out);
+  return hipGetLastError();
+}
+
 template <int D>
-hipError_t launch_d(const void* q, int64_t T, int64_t q_pos0, int H, float scale_log2,
-                    const void* raw, int64_t raw_pos0, int window, const void* pooled,
-                    const int32_t* sel, int topk, void* out, hipStream_t s) {
+hipError_t launch_d(const void* q, int64_t T, int64_t q_pos0, int H, float sl2, const void* raw,
+                    int64_t raw_pos0, int window, const void* pooled, const int32_t* sel,
+                    int topk, void* out, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(T));
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* rr = static_cast<const uint16_t*>(raw);
   const auto* pp = static_cast<const uint16_t*>(pooled);
   auto* oo = static_cast<uint16_t*>(out);
-  const int nw = (H + 15) / 16;
-  switch (nw) {
-    case 1: hipLaunchKernelGGL((sparse_attn_kernel<D, 1>), grid, dim3(64), 0, s, qq, q_pos0, H, scale_log2, rr, raw_pos0, window, pp, sel, topk, oo); break;
-    case 2: hipLaunchKernelGGL((sparse_attn_kernel<D, 2>), grid, dim3(128), 0, s, qq, q_pos0, H, scale_log2, rr, raw_pos0, window, pp, sel, topk, oo); break;
-    case 3: hipLaunchKernelGGL((sparse_attn_kernel<D, 3>), grid, dim3(192), 0, s, qq, q_pos0, H, scale_log2, rr, raw_pos0, window, pp, sel, topk, oo); break;
-    default: hipLaunchKernelGGL((sparse_attn_kernel<D, 4>), grid, dim3(256), 0, s, qq, q_pos0, H, scale_log2, rr, raw_pos0, window, pp, sel, topk, oo); break;
+  const size_t dyn = static_cast<size_t>(sel ? topk : 0) * sizeof(int);
+  switch ((H + 15) / 16) {
+    case 1: return launch_hg<D, 1>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, sel, topk, oo);
+    case 2: return launch_hg<D, 2>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, sel, topk, oo);
+    case 3: return launch_hg<D, 3>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, sel, topk, oo);
+    default: return launch_hg<D, 4>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, sel, topk, oo);
   }
-  return hipGetLastError();
 }
 
 }  // namespace
