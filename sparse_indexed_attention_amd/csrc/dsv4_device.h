@@ -51,6 +51,26 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 // Pooled rows visible to a query at absolute position p (ratio 4).
 __device__ __forceinline__ int64_t visible_rows(int64_t p) { return (p + 1) >> 2; }
 
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane L of the wave writes lds_wave_base + 16*L.
+// Issued as inline asm so the compiler neither reorders it nor adds its own
+// conservative vmcnt(0) waits for it; callers wait with s_waitcnt vmcnt before
+// the barrier that publishes the data.  Issued after the compiler's own loads,
+// these can only make the compiler's in-order vmcnt waits stricter.
+__device__ __forceinline__ void global_to_lds16(const void* g, const void* lds_wave_base) {
+  const uint32_t lds = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_wave_base));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
+// s_waitcnt immediates (gfx9 encoding): vmcnt(n) with the other counters open,
+// and lgkmcnt(0) with the others open.
+constexpr int kWaitVm0 = 0x0F70;
+__device__ __forceinline__ constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
 }  // namespace dsv4
 
 // Launch wrappers (defined next to their kernels).  All return hipError_t of

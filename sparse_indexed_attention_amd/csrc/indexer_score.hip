@@ -49,18 +49,6 @@ constexpr int kQB = kWaves * kQW;      // queries per workgroup
 constexpr int kTileCols = 64;          // key rows per LDS tile
 constexpr int kStages = 3;
 
-__device__ __forceinline__ void global_to_lds16(const void* g, const void* lds_wave_base) {
-  // 16 bytes per lane from global memory straight into LDS (lane L writes
-  // lds_wave_base + 16*L).  Inline asm: the compiler neither reorders it nor
-  // adds its own conservative waits; the kernel waits with s_waitcnt vmcnt.
-  const uint32_t lds = static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_wave_base));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "m0");
-}
-
 template <int KSTEPS, int MT>
 __global__ void __launch_bounds__(kThreads, 2)
 indexer_score_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,

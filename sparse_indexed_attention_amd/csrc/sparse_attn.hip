@@ -55,20 +55,6 @@ constexpr int kStages = 3;  // LDS tile stages: two tiles in flight while one is
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-// 16 bytes per lane from global memory straight into LDS: lane L of the wave
-// writes lds_wave_base + 16*L.  Issued as inline asm so the compiler neither
-// reorders it nor adds its own (conservative, vmcnt(0)) waits for it: the
-// kernel waits for these loads itself with s_waitcnt vmcnt before the barrier
-// that publishes a tile.  Being issued after the compiler's own loads, they
-// can only make the compiler's in-order vmcnt waits stricter, never weaker.
-__device__ __forceinline__ void global_to_lds16(const void* g, const void* lds_wave_base) {
-  const uint32_t lds = static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_wave_base));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "m0");
-}
 
 template <int D, int NHG, int DSPLIT>
 __global__ void __launch_bounds__(NHG * DSPLIT * 64)
