@@ -135,7 +135,8 @@ int dsv4_compress(dsv4_pool_cache* cache, const void* x, int64_t n_new, void* st
  * pooled-ratio causal mask folded into the score epilogue [P2 commit 5]);
  * fold_mask = 0: every s < S is scored (second-pass masking is then the
  * caller's, with the same -inf sentinel).
- * Shape gate: bf16 cache, dim in {32, 64, 128}, 1 <= n_heads <= 64.
+ * Shape gate: bf16 cache, dim in {32, 64, 128}, 1 <= n_heads <= 64,
+ * S <= out_stride <= 2^28 - 64 (UNSUPPORTED beyond).
  */
 int dsv4_indexer_scores(const dsv4_pool_cache* index_cache, const void* q, const float* w,
                         int64_t rows, int64_t q_pos0, int32_t n_heads, int32_t fold_mask,

@@ -117,6 +117,9 @@ static int check_scores_args(const dsv4_pool_cache* ic, const void* q, const flo
   if (rows > 0 && (!q || !w)) return fail(DSV4_ERR_INVALID_ARG, "%s: NULL q or w", who);
   if (rows > 0 && (!aligned16(q) || !aligned16(ic->rows)))
     return fail(DSV4_ERR_INVALID_ARG, "%s: q and cache rows must be 16-byte aligned", who);
+  if (ic->n_rows > dsv4::kMaxScoreStride)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: %lld pooled rows (at most %lld)", who,
+                (long long)ic->n_rows, (long long)dsv4::kMaxScoreStride);
   const int64_t frontier = 4 * ic->n_rows + ic->n_rem;
   if (q_pos0 + rows > frontier)
     return fail(DSV4_ERR_INVALID_ARG,
@@ -133,6 +136,9 @@ int dsv4_indexer_scores(const dsv4_pool_cache* index_cache, const void* q, const
   const int64_t S = index_cache->n_rows;
   if (rows > 0 && S > 0 && !out) return fail(DSV4_ERR_INVALID_ARG, "indexer_scores: NULL out");
   if (out_stride < S) return fail(DSV4_ERR_INVALID_ARG, "indexer_scores: stride < rows of cache");
+  if (out_stride > dsv4::kMaxScoreStride)
+    return fail(DSV4_ERR_UNSUPPORTED, "indexer_scores: stride %lld (at most %lld)",
+                (long long)out_stride, (long long)dsv4::kMaxScoreStride);
   if (rows == 0 || S == 0) return DSV4_OK;
   return hip_status(dsv4_launch_indexer_scores(q, w, index_cache->rows, rows, q_pos0, S, n_heads,
                                                index_cache->dim, fold_mask ? 1 : 0, out,

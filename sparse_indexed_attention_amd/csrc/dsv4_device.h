@@ -48,6 +48,17 @@ __device__ __forceinline__ uint32_t float_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// max(x, 0) on the float's bits: one integer max, no NaN canonicalisation.
+// Equal to fmaxf(x, 0) for every non-NaN x (-0 gives +0).
+__device__ __forceinline__ float relu_bits(float x) {
+  const int32_t i = __float_as_int(x);
+  return __int_as_float(i > 0 ? i : 0);
+}
+
+// Largest score-row stride (floats) the score kernel accepts: two rows of it
+// must fit a 32-bit buffer range.
+constexpr int64_t kMaxScoreStride = (int64_t(1) << 28) - 64;
+
 // Pooled rows visible to a query at absolute position p (ratio 4).
 __device__ __forceinline__ int64_t visible_rows(int64_t p) { return (p + 1) >> 2; }
 
@@ -63,6 +74,18 @@ __device__ __forceinline__ void global_to_lds16(const void* g, const void* lds_w
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
+// Same, addressed as a wave-uniform 64-bit base (SGPR pair) plus a 32-bit
+// per-lane byte offset (the saddr form of the instruction).
+__device__ __forceinline__ void global_to_lds16_s(const void* sbase, uint32_t voff,
+                                                  const void* lds_wave_base) {
+  const uint32_t lds = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_wave_base));
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
 
