@@ -41,11 +41,14 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 }
 
 // Order-preserving unsigned key of a float: a < b  <=>  key(a) < key(b) for
-// non-NaN inputs; -0 and +0 map to the same key.
+// non-NaN inputs; -0 and +0 map to the same key (adding +0 turns -0 into +0
+// and leaves every other non-NaN value unchanged).  Negative floats have all
+// bits flipped, non-negative ones only the sign bit; no non-NaN float maps
+// to key 0.
 __device__ __forceinline__ uint32_t float_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;  // -0 -> +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  const uint32_t neg = static_cast<uint32_t>(static_cast<int32_t>(u) >> 31);
+  return u ^ (neg | 0x80000000u);
 }
 
 // max(x, 0) on the float's bits: one integer max, no NaN canonicalisation.

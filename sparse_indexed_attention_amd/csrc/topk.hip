@@ -15,15 +15,21 @@
 //     global_load_lds_dwordx4 while the current item is processed, so HBM
 //     reads overlap all the compute below.  Thread t holds columns
 //     [PER*t, PER*t + PER) of the item in registers as order-preserving 32-bit
-//     keys.
-//   * MSB-first radix select with 11-bit digits starting at the highest bit
-//     in which the item's max and min keys differ (all keys share the bits
-//     above it); one LDS histogram (2,048 bins) per pass gives the exact
+//     keys; their max and min are reduced while the keys are made.
+//   * Threshold: MSB-first radix select with 11-bit digits starting at the
+//     highest bit in which the item's max and min keys differ (all keys share
+//     the bits above it).  One LDS histogram (2,048 bins) locates the digit of
+//     the k-th key; the keys of that bin (usually a few dozen) are then copied
+//     to an LDS list and one wave finishes the remaining bits with ballot
+//     counts, without further workgroup barriers.  A bin too large for the
+//     list takes further histogram passes instead.  The result is the exact
 //     threshold key T and the number of T-valued keys still needed.
-//   * Ordered emission: each thread counts its keys > T and == T, one block
-//     scan turns the counts into offsets, and each chosen key lands at
-//     (#greater before it) + min(#equal before it, needed equal): ascending
-//     output, ties to the lower column.
+//   * Ordered emission: each thread counts its keys > T and == T (packed in
+//     one word), one block scan turns the counts into offsets, and each chosen
+//     key lands at (#greater before it) + min(#equal before it, needed
+//     equal): ascending output, ties to the lower column.
+//   * Wave-level scans and reductions use DPP row shifts and row broadcasts
+//     (no LDS round trips).
 //   * Long rows: a tournament over chunks.  The running top-k (at most k keys
 //     and columns, ascending) stays in LDS and precedes the next chunk in the
 //     same ordered selection; the top-k of (carry ++ chunk) is the top-k of
@@ -37,24 +43,45 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 2048;                    // 11-bit digits
+constexpr int kCandCap = 1024;                 // keys of one bin finished without more passes
+constexpr int kRankCap = 256;                  // ... by direct ranking (else bit by bit)
 
-template <typename F>
-__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, F op) {
-  for (int off = 32; off > 0; off >>= 1)
-    v = op(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off)));
-  return v;
+// DPP move with 0 in lanes whose source is outside the pattern.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_or0(uint32_t x) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, ROW_MASK, 0xF, false));
 }
 
-// Exclusive scan over the workgroup in thread order; `scr` holds kWaves
-// entries.  *total receives the sum.
+// Inclusive prefix sum over the 64 lanes: row_shr 1, 2, 4, 8 within each
+// 16-lane row, then lane 15 into rows 1 and 3 and lane 31 into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_or0<0x111, 0xF>(x);
+  x += dpp_or0<0x112, 0xF>(x);
+  x += dpp_or0<0x114, 0xF>(x);
+  x += dpp_or0<0x118, 0xF>(x);
+  x += dpp_or0<0x142, 0xA>(x);
+  x += dpp_or0<0x143, 0xC>(x);
+  return x;
+}
+
+// Maximum over the 64 lanes (same pattern; lane 63 ends with the result).
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = max(x, dpp_or0<0x111, 0xF>(x));
+  x = max(x, dpp_or0<0x112, 0xF>(x));
+  x = max(x, dpp_or0<0x114, 0xF>(x));
+  x = max(x, dpp_or0<0x118, 0xF>(x));
+  x = max(x, dpp_or0<0x142, 0xA>(x));
+  x = max(x, dpp_or0<0x143, 0xC>(x));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
+
+// Exclusive scan over the workgroup in thread order (one barrier); `scr`
+// holds kWaves entries.  *total receives the sum.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scr,
                                                          uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = static_cast<uint32_t>(__shfl_up(static_cast<int>(incl), off));
-    if (lane >= off) incl += y;
-  }
+  const uint32_t incl = wave_incl_scan(v);
   if (lane == 63) scr[wave] = incl;
   __syncthreads();
   uint32_t before = 0, all = 0;
@@ -105,16 +132,20 @@ __device__ __forceinline__ int chunk_slot(int c) {
   return i * 64 + 8 * (a ^ (i & 1)) + ((lp & 7) ^ a);
 }
 
-// Copy the whole 16-byte chunks of item columns [0, n) to LDS `buf` in the
-// chunk_slot order (the tail of fewer than 4 columns is read from global
-// memory later).  Wave w issues the 1 KiB blocks w, w + 16, ...; lane L of
-// block i writes slot 64i + L and fetches the chunk that maps there; a lane
-// whose chunk lies past the last whole chunk re-reads the block's first chunk
-// (always valid) and its bytes are never used.
-__device__ __forceinline__ void issue_item(const float* src, int n, float* buf) {
-  const int n4 = n & ~3;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int i = wave; i * 256 < n4; i += kWaves) {
+// Copy the 16-byte chunks covering item columns [0, n) to LDS `buf` in the
+// chunk_slot order.  A partial last chunk is copied whole: rows are allocated
+// `stride` floats with stride % 4 == 0, so its columns past n are in bounds
+// (their values are never used).  Wave w issues the 1 KiB blocks w, w + 16,
+// ...; lane L of block i writes slot 64i + L and fetches the chunk that maps
+// there; a lane whose chunk lies past the last one re-reads the block's first
+// chunk (always valid) and its bytes are never used.
+// `half` selects every other block of the wave (0: w, w + 32, ...; 1: w + 16,
+// w + 48, ...), so an item can be issued in two parts.
+__device__ __forceinline__ void issue_item(const float* src, int n, float* buf, int wave,
+                                           int half) {
+  const int n4 = (n + 3) & ~3;
+  const int lane = threadIdx.x & 63;
+  for (int i = wave + half * kWaves; i * 256 < n4; i += 2 * kWaves) {
     const int a = ((lane >> 3) & 7) ^ (i & 1);
     const int lp = 8 * a + ((lane & 7) ^ a);
     const int e = i * 256 + 4 * lp;
@@ -132,24 +163,47 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
   constexpr int KMAX = CPT > 0 ? CPT * kThreads : 1;
   constexpr int kPer = PER;
   constexpr int kChunk = PER * kThreads;
+  constexpr int kCE = kCandCap / 64;  // list entries per lane of the finishing wave
+  // Histogram + candidate list while the threshold is found, then the item's
+  // output row staged for one coalesced copy (top-k <= 2,048 for CPT == 2,
+  // which keeps that variant inside 160 KiB of LDS).
+  // With a single chunk per row (CPT == 0) the output row has its own area
+  // and is copied out at the start of the next item, after the end-of-item
+  // barrier; otherwise it reuses the work area.
+  constexpr bool kSepOut = CPT == 0;
+  constexpr int kWork = kSepOut ? kBins + kCandCap : (CPT == 2 ? kBins + kCandCap : 4096);
+  static_assert(kWork >= kBins + kCandCap, "work area");
   __shared__ __attribute__((aligned(16))) float rowbuf[kChunk];
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t scr[4][kWaves];
-  __shared__ uint32_t s_red[2][kWaves];
-  __shared__ uint32_t s_bin, s_cum;
+  __shared__ __attribute__((aligned(16))) uint32_t work[kWork];
+  __shared__ int32_t out_sep[kSepOut ? 4096 : 1];
+  uint32_t* const hist = work;
+  uint32_t* const cand = work + kBins;
+  int32_t* const obuf = kSepOut ? out_sep : reinterpret_cast<int32_t*>(work);
+  int64_t pend_row = -1;  // row whose staged output awaits its copy (kSepOut)
+  int pend_need = 0;
+  auto copy_out = [&](int64_t row, int nsel) {
+    int32_t* d = out_idx + row * static_cast<int64_t>(topk);
+    for (int j = static_cast<int>(threadIdx.x); j < topk; j += kThreads) d[j] = j < nsel ? obuf[j] : -1;
+  };
+  __shared__ uint32_t scr[2][kWaves];
+  __shared__ uint32_t s_red[4][kWaves];
+  __shared__ uint32_t s_bin, s_cum, s_cnt, s_ncand, s_T, s_rem;
   __shared__ uint32_t ckey[KMAX];
   __shared__ int32_t cidx[KMAX];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t g = blockIdx.x, G = gridDim.x;
 
   uint32_t key[kPer];
   Item cur, nx;
   int64_t it = 0;
   if (!item_of<kChunk>(it, rows, q_pos0, g, G, chunks_per_row, &cur)) return;
-  if (DMA) issue_item(scores + cur.row * stride + cur.base, cur.n, rowbuf);
+  if (DMA) {
+    issue_item(scores + cur.row * stride + cur.base, cur.n, rowbuf, wave, 0);
+    issue_item(scores + cur.row * stride + cur.base, cur.n, rowbuf, wave, 1);
+  }
   int c = 0;  // carry entries of the current row
 
   while (true) {
@@ -159,37 +213,60 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
     }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of the item landed
     __syncthreads();                       // ... and every other wave's
+    // Only the wave holding the item's end has columns past it; every other
+    // wave skips the validity tests (uniform branches on wave_full).
+    const bool wave_full = (wave * 64 + 63) * kPer + kPer <= cur.n;
+    const int lim = cur.n - tid * kPer;  // valid columns of this thread (if < kPer)
     {
-      // keys; 0 marks a column past the item's end (no float maps to key 0)
-      const float* src = scores + cur.row * stride + cur.base;
-      const int n4 = DMA ? (cur.n & ~3) : cur.n;
+      // keys; 0 marks a column past the item's end (no float maps to key 0).
+      // Every thread reads its PER columns with vector reads (always inside
+      // the row buffer); only the wave holding the item's end masks them.
       const int e0 = tid * kPer;
-      if (e0 + kPer <= n4) {
 #pragma unroll
-        for (int v = 0; v < kPer / 4; ++v) {
-          const int slot = DMA ? chunk_slot((e0 >> 2) + v) : (e0 >> 2) + v;
-          const float4 x = *reinterpret_cast<const float4*>(&rowbuf[4 * slot]);
-          key[4 * v] = float_key(x.x);
-          key[4 * v + 1] = float_key(x.y);
-          key[4 * v + 2] = float_key(x.z);
-          key[4 * v + 3] = float_key(x.w);
+      for (int v = 0; v < kPer / 4; ++v) {
+        const int slot = DMA ? chunk_slot((e0 >> 2) + v) : (e0 >> 2) + v;
+        const float4 x = *reinterpret_cast<const float4*>(&rowbuf[4 * slot]);
+        key[4 * v] = float_key(x.x);
+        key[4 * v + 1] = float_key(x.y);
+        key[4 * v + 2] = float_key(x.z);
+        key[4 * v + 3] = float_key(x.w);
+      }
+      // the item's key range, reduced per wave now (published by the barrier
+      // below); min over valid keys is max over their complements
+      uint32_t kmax = 0u, nmin = 0u;
+      if (wave_full) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          kmax = max(kmax, key[j]);
+          nmin = max(nmin, ~key[j]);
         }
       } else {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-          const int e = e0 + j;
-          const int at = DMA ? 4 * chunk_slot(e >> 2) + (e & 3) : e;
-          const float f = (e < n4) ? rowbuf[at] : ((e < cur.n) ? src[e] : 0.f);
-          key[j] = (e < cur.n) ? float_key(f) : 0u;
+          key[j] = j < lim ? key[j] : 0u;
+          kmax = max(kmax, key[j]);
+          nmin = max(nmin, j < lim ? ~key[j] : 0u);
         }
       }
+      kmax = wave_max(kmax);
+      nmin = wave_max(nmin);
+      if (lane == 0) { s_red[0][wave] = kmax; s_red[1][wave] = nmin; }
+      // the first histogram pass's table, cleared ahead of the barrier
+      for (int i = tid; i < kBins; i += kThreads) hist[i] = 0u;
+      if (tid == 0) s_ncand = 0u;
     }
     const bool have_next = item_of<kChunk>(it + 1, rows, q_pos0, g, G, chunks_per_row, &nx);
     __syncthreads();  // every thread has its keys: the row buffer takes the next item
-    if (DMA && have_next) issue_item(scores + nx.row * stride + nx.base, nx.n, rowbuf);
+    if (DMA && have_next) issue_item(scores + nx.row * stride + nx.base, nx.n, rowbuf, wave, 0);
+    bool second_half = DMA && have_next;  // the rest of the next item's copy, issued later
+    if (kSepOut && pend_row >= 0) {
+      copy_out(pend_row, pend_need);  // the previous item's staged row
+      pend_row = -1;
+    }
     if (cur.first) c = 0;
     // chunk slots past a shorter row's end carry no work (uniform branch)
     if (!cur.first && cur.n == 0) {
+      if (second_half) issue_item(scores + nx.row * stride + nx.base, nx.n, rowbuf, wave, 1);
       if (!have_next) break;
       cur = nx;
       ++it;
@@ -213,24 +290,32 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
     const int E = c + n;
     const int need = E < topk ? E : topk;
     uint32_t T = 0u, need_eq = 0u;  // need == E: every valid key (> 0) is chosen
+    if (second_half && !(need < E)) {
+      issue_item(scores + nx.row * stride + nx.base, nx.n, rowbuf, wave, 1);
+      second_half = false;
+    }
 
     if (need < E) {
-      uint32_t kmax = 0u, kmin = 0xffffffffu;
+      if (CPT > 0) {
+        uint32_t kmax = 0u, nmin = 0u;
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        kmax = max(kmax, key[j]);
-        kmin = min(kmin, key[j] ? key[j] : 0xffffffffu);
+        for (int j = 0; j < (CPT > 0 ? CPT : 0); ++j) {
+          kmax = max(kmax, ck[j]);
+          nmin = max(nmin, ck[j] ? ~ck[j] : 0u);
+        }
+        kmax = wave_max(kmax);
+        nmin = wave_max(nmin);
+        if (lane == 0) { s_red[2][wave] = kmax; s_red[3][wave] = nmin; }
+        __syncthreads();
       }
+      uint32_t mx = 0u, nmn = 0u;
 #pragma unroll
-      for (int j = 0; j < (CPT > 0 ? CPT : 0); ++j)
-        if (j < cv) { kmax = max(kmax, ck[j]); kmin = min(kmin, ck[j]); }
-      kmax = wave_reduce(kmax, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
-      kmin = wave_reduce(kmin, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
-      if (lane == 0) { s_red[0][wave] = kmax; s_red[1][wave] = kmin; }
-      __syncthreads();
-      uint32_t mx = 0u, mn = 0xffffffffu;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) { mx = max(mx, s_red[0][w]); mn = min(mn, s_red[1][w]); }
+      for (int w = 0; w < kWaves; ++w) {
+        mx = max(mx, s_red[0][w]);
+        nmn = max(nmn, s_red[1][w]);
+        if (CPT > 0) { mx = max(mx, s_red[2][w]); nmn = max(nmn, s_red[3][w]); }
+      }
+      const uint32_t mn = ~nmn;
 
       uint32_t remaining = static_cast<uint32_t>(need);
       uint32_t prefix, mask;
@@ -245,19 +330,37 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
         prefix = mx & mask;
         shift = hb + 1;
       }
+      bool first_pass = true;
       while (shift > 0) {
         const int dbits = shift < 11 ? shift : 11;
         shift -= dbits;
         const uint32_t dmask = (1u << dbits) - 1u;
-        for (int i = tid; i < kBins; i += kThreads) hist[i] = 0u;
-        __syncthreads();
+        if (!first_pass) {
+          for (int i = tid; i < kBins; i += kThreads) hist[i] = 0u;
+          if (tid == 0) s_ncand = 0u;
+          __syncthreads();
+        }
+        // every valid key shares the max/min prefix, so the first pass counts
+        // all of them
+        if (first_pass && wave_full) {
 #pragma unroll
-        for (int j = 0; j < kPer; ++j)
-          if (key[j] != 0u && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
+          for (int j = 0; j < kPer; ++j) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
+        } else {
+#pragma unroll
+          for (int j = 0; j < kPer; ++j)
+            if (j < lim && (first_pass || (key[j] & mask) == prefix))
+              atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
+        }
 #pragma unroll
         for (int j = 0; j < (CPT > 0 ? CPT : 0); ++j)
-          if (j < cv && (ck[j] & mask) == prefix) atomicAdd(&hist[(ck[j] >> shift) & dmask], 1u);
+          if (j < cv && (first_pass || (ck[j] & mask) == prefix))
+            atomicAdd(&hist[(ck[j] >> shift) & dmask], 1u);
+        first_pass = false;
         __syncthreads();
+        if (second_half) {
+          issue_item(scores + nx.row * stride + nx.base, nx.n, rowbuf, wave, 1);
+          second_half = false;
+        }
         if (wave == 0) {
           // lane l owns bins 32l .. 32l+31 as 8 groups of 4; suffix sums over
           // lanes locate the lane, then the group, then the bin
@@ -269,11 +372,11 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
             gs[v] = q4[0] + q4[1] + q4[2] + q4[3];
             own += gs[v];
           }
-          uint32_t incl = own;
-          for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t y = static_cast<uint32_t>(__shfl_down(static_cast<int>(incl), off));
-            if (lane + off < 64) incl += y;
-          }
+          // bins of lanes >= this one: the total minus the exclusive prefix
+          const uint32_t pre = wave_incl_scan(own);
+          const uint32_t all =
+              static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(pre), 63));
+          const uint32_t incl = all - pre + own;
           const uint32_t above = incl - own;
           if (above < remaining && remaining <= incl) {
             uint32_t cum = above;
@@ -292,12 +395,93 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
             }
             s_bin = static_cast<uint32_t>(32 * lane + 4 * gv + b);
             s_cum = cum;
+            s_cnt = q4[b];
           }
         }
         __syncthreads();
         remaining -= s_cum;
         prefix |= s_bin << shift;
         mask |= dmask << shift;
+        const uint32_t in_bin = s_cnt;  // keys sharing the digits so far; remaining <= in_bin
+        if (shift > 0 && in_bin <= static_cast<uint32_t>(kCandCap)) {
+          // ---- finish: list the bin's keys, one wave resolves the low bits
+          uint32_t mk = 0;
+#pragma unroll
+          for (int j = 0; j < kPer; ++j)
+            mk |= static_cast<uint32_t>((key[j] & mask) == prefix) << j;
+          if (!wave_full) mk &= lim >= kPer ? 0xffffffffu : (lim > 0 ? (1u << lim) - 1u : 0u);
+          uint32_t mc = 0;
+#pragma unroll
+          for (int j = 0; j < (CPT > 0 ? CPT : 0); ++j)
+            mc |= static_cast<uint32_t>(j < cv && (ck[j] & mask) == prefix) << j;
+          const uint32_t cnt = __popc(mk) + __popc(mc);
+          if (cnt) {
+            uint32_t pos = atomicAdd(&s_ncand, cnt);
+            // the matches number exactly in_bin <= kCandCap; the guard only
+            // keeps the writes inside the list
+#pragma unroll
+            for (int j = 0; j < kPer; ++j)
+              if (((mk >> j) & 1u) && pos < kCandCap) cand[pos++] = key[j];
+#pragma unroll
+            for (int j = 0; j < (CPT > 0 ? CPT : 0); ++j)
+              if (((mc >> j) & 1u) && pos < kCandCap) cand[pos++] = ck[j];
+          }
+          __syncthreads();
+          if (in_bin <= static_cast<uint32_t>(kRankCap)) {
+            // thread i ranks list entry i against the whole list (broadcast
+            // reads); the entry with #greater < remaining <= #greater-or-equal
+            // is the threshold (equal entries write equal values)
+            if (static_cast<uint32_t>(tid) < in_bin) {
+              const uint32_t x = cand[tid];
+              uint32_t gt = 0, ge = 0;
+              for (uint32_t m4 = 0; m4 < in_bin; m4 += 4) {
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&cand[m4]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const bool ok = m4 + i < in_bin;
+                  gt += ok && v[i] > x;
+                  ge += ok && v[i] >= x;
+                }
+              }
+              if (gt < remaining && remaining <= ge) { s_T = x; s_rem = remaining - gt; }
+            }
+          } else if (wave == 0) {
+            // larger lists: one wave settles the low bits one at a time with
+            // ballot counts
+            uint32_t x[kCE];
+            uint32_t alive = 0u;  // bit e: entry lane + 64e is still a candidate
+#pragma unroll
+            for (int e = 0; e < kCE; ++e) {
+              const uint32_t idx = static_cast<uint32_t>(lane + 64 * e);
+              x[e] = idx < in_bin ? cand[idx] : 0u;
+              alive |= static_cast<uint32_t>(idx < in_bin) << e;
+            }
+            uint32_t pfx = prefix, rem = remaining;
+            for (int b = shift - 1; b >= 0; --b) {
+              uint32_t ones = 0u;  // alive entries with bit b set
+              uint32_t c1 = 0u;
+#pragma unroll
+              for (int e = 0; e < kCE; ++e) {
+                if (64u * e >= in_bin) break;  // uniform
+                const bool one = ((alive >> e) & 1u) && ((x[e] >> b) & 1u);
+                ones |= static_cast<uint32_t>(one) << e;
+                c1 += static_cast<uint32_t>(__popcll(__ballot(one)));
+              }
+              if (c1 >= rem) {
+                pfx |= 1u << b;
+                alive = ones;
+              } else {
+                rem -= c1;
+                alive &= ~ones;
+              }
+            }
+            if (lane == 0) { s_T = pfx; s_rem = rem; }
+          }
+          __syncthreads();
+          prefix = s_T;
+          remaining = s_rem;
+          shift = 0;
+        }
       }
       T = prefix;
       need_eq = remaining;
@@ -314,27 +498,27 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
       gtm |= static_cast<uint32_t>(key[j] > T) << j;
       eqm |= static_cast<uint32_t>(key[j] == T) << j;  // key 0 only equals T = 0 (need_eq = 0)
     }
-    const uint32_t k_gt = __popc(gtm), k_eq = __popc(eqm);
-    uint32_t tot_cgt = 0, tot_ceq = 0, tot_kgt, tot_keq;
-    uint32_t cgt_b = 0, ceq_b = 0;
-    if (CPT > 0) {
-      cgt_b = block_exclusive_scan(c_gt, scr[0], &tot_cgt);
-      ceq_b = block_exclusive_scan(c_eq, scr[1], &tot_ceq);
-    }
-    const uint32_t kgt_b = block_exclusive_scan(k_gt, scr[2], &tot_kgt) + tot_cgt;
-    const uint32_t keq_b = block_exclusive_scan(k_eq, scr[3], &tot_keq) + tot_ceq;
-    int32_t* dst = out_idx + cur.row * static_cast<int64_t>(topk);
+    // counts packed as (greater | equal << 16): each total is at most
+    // carry + chunk < 65,536
+    uint32_t tot_c = 0, tot_k;
+    uint32_t cb = 0;
+    if (CPT > 0) cb = block_exclusive_scan(c_gt | (c_eq << 16), scr[0], &tot_c);
+    const uint32_t kb = block_exclusive_scan(
+        static_cast<uint32_t>(__popc(gtm)) | (static_cast<uint32_t>(__popc(eqm)) << 16), scr[1],
+        &tot_k);
+    const uint32_t kgt_b = (kb & 0xffffu) + (tot_c & 0xffffu);
+    const uint32_t keq_b = (kb >> 16) + (tot_c >> 16);
     const bool to_out = (CPT == 0) || cur.last;
     if (CPT > 0) {
       // carry entries (at most CPT per thread)
-      uint32_t gtb = cgt_b, eqb = ceq_b;
+      uint32_t gtb = cb & 0xffffu, eqb = cb >> 16;
 #pragma unroll
       for (int j = 0; j < (CPT > 0 ? CPT : 0); ++j) {
         if (j < cv) {
           const bool gt = ck[j] > T, eq = ck[j] == T;
           if (gt || (eq && eqb < need_eq)) {
             const uint32_t pos = gtb + (eqb < need_eq ? eqb : need_eq);
-            if (to_out) dst[pos] = ci[j];
+            if (to_out) obuf[pos] = ci[j];
             else { ckey[pos] = ck[j]; cidx[pos] = ci[j]; }
           }
           gtb += gt;
@@ -353,7 +537,7 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
         const bool gt = (gtm >> j) & 1u;
         const uint32_t eqb = keq_b + __popc(eqm & low);
         if (gt || eqb < need_eq) {
-          dst[kgt_b + __popc(gtm & low) + (eqb < need_eq ? eqb : need_eq)] = col0 + j;
+          obuf[kgt_b + __popc(gtm & low) + (eqb < need_eq ? eqb : need_eq)] = col0 + j;
         } else {
           m &= gtm;  // later equal keys rank even lower
         }
@@ -373,13 +557,23 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
       }
     }
     c = need;
-    if (cur.last) {
-      const int64_t vis = visible_rows(q_pos0 + cur.row);
-      const int64_t k_total = vis < topk ? vis : topk;
-      for (int64_t j = k_total + tid; j < topk; j += kThreads) dst[j] = -1;
+    if (to_out) {
+      // the row's min(k, visible) choices (need of them) are staged in LDS;
+      // they are copied out coalesced and padded with -1 once every thread's
+      // writes are in: after the next barrier (kSepOut: at the next item)
+      if (kSepOut) {
+        pend_row = cur.row;
+        pend_need = need;
+      } else {
+        __syncthreads();
+        copy_out(cur.row, need);
+      }
     }
     __syncthreads();  // LDS tables / carry reused by the next item
-    if (!have_next) break;
+    if (!have_next) {
+      if (kSepOut && pend_row >= 0) copy_out(pend_row, pend_need);
+      break;
+    }
     cur = nx;
     ++it;
   }
