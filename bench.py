@@ -17,6 +17,14 @@ its own launches in the same configuration; `cpu_baseline` times the CPU
 oracle on a bounded sample of the same workload's query rows.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-seconds S]
+
+`roofline.traffic` (HBM bytes per score-kernel launch) comes from the
+rocprofv3 counter summary profiles/traffic_indexer_score_<workload>.md and is
+reported only while the score kernel's sources still hash to the value
+recorded there (otherwise null).  That summary is made by two counter runs of
+this script with --calibration-copy (FETCH_SIZE, then WRITE_SIZE) and
+`bench.py --summarize-pmc FETCH_DB WRITE_DB OUT_MD --workload NAME`; the
+calibration copy scales each counter to bytes.
 """
 from __future__ import annotations
 
@@ -29,10 +37,104 @@ import time
 import numpy as np
 import torch
 
-import synthetic_inputs as SI
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synthetic_inputs as SI  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+COPY_BYTES = 1 << 30        # the calibration copy kernel moves this many bytes each way
+SCORE_SOURCES = ("sparse_indexed_attention_amd/csrc/indexer_score.hip",
+                 "sparse_indexed_attention_amd/csrc/dsv4_device.h")
+SCORE_KERNEL = "indexer_score_kernel"
+
+
+def score_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in SCORE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_indexer_score_{workload}.md")
+
+
+def recorded_traffic(workload: str):
+    """Bytes per score launch from the counter summary, if its source hash matches."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("score_source_hash") != score_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize_pmc(fetch_db: str, write_db: str, out_md: str, workload: str, cmds: str):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE of the score kernel, scaled to bytes
+    by what the same counters read for the 1 GiB calibration copy."""
+    import sqlite3
+
+    def per_dispatch(db, counter):
+        c = sqlite3.connect(db)
+        rows = c.execute(
+            "select name, dispatch_id, sum(counter_value) from pmc_events "
+            "where counter_name = ? group by name, dispatch_id", (counter,)).fetchall()
+        score = [v for n, _, v in rows if SCORE_KERNEL in n]
+        copy = [v for n, _, v in rows if "elementwise" in n.lower()]
+        return score, copy
+
+    fs, fc = per_dispatch(fetch_db, "FETCH_SIZE")
+    ws, wc = per_dispatch(write_db, "WRITE_SIZE")
+    if not (fs and ws and fc and wc):
+        raise SystemExit("summarize-pmc: score or copy dispatches missing from the databases")
+    # the copy's largest dispatches are the 1 GiB calibration copies
+    fc, wc = sorted(fc)[-3:], sorted(wc)[-3:]
+    k_fetch = np.mean(fc) * 1024.0 / COPY_BYTES   # counter KiB per byte actually moved
+    k_write = np.mean(wc) * 1024.0 / COPY_BYTES
+    fetch_b = np.mean(fs) * 1024.0 / k_fetch
+    write_b = np.mean(ws) * 1024.0 / k_write
+    wl = SI.WORKLOADS[workload]
+    T = wl.chunk
+    pairs = sum((p + 1) // 4 for p in range(wl.q_pos0, wl.q_pos0 + T))
+    S = (wl.q_pos0 + T) // 4
+    algo = S * wl.idx_dim * 2 + T * wl.idx_heads * (wl.idx_dim * 2 + 4) + T * S * 4
+    with open(out_md, "w") as fh:
+        fh.write(f"# HBM traffic of the indexer score kernel, {workload}\n\n")
+        fh.write("Counters: rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each in its own\n"
+                 "run, summed over instances per dispatch and averaged over the score kernel's\n"
+                 "dispatches; each scaled by what the same counter reads for a plain copy kernel of\n"
+                 "known size in the same process (--calibration-copy: a torch elementwise negate\n"
+                 "that reads 1 GiB and writes 1 GiB).\n\n")
+        fh.write("Commands:\n\n```\n" + cmds.strip() + "\n```\n\n")
+        fh.write(f"- workload: `{workload}`\n")
+        fh.write(f"- score_source_hash: `{score_source_hash()}`\n")
+        fh.write(f"- score_dispatches: {len(fs)} (fetch run), {len(ws)} (write run)\n")
+        fh.write(f"- copy_fetch_kib_per_gib: {np.mean(fc):.1f}\n")
+        fh.write(f"- copy_write_kib_per_gib: {np.mean(wc):.1f}\n")
+        fh.write(f"- fetch_scale: {k_fetch:.4f}\n")
+        fh.write(f"- write_scale: {k_write:.4f}\n")
+        fh.write(f"- score_fetch_kib_raw: {np.mean(fs):.1f}\n")
+        fh.write(f"- score_write_kib_raw: {np.mean(ws):.1f}\n")
+        fh.write(f"- hbm_fetch_bytes_per_launch: {fetch_b:.0f}\n")
+        fh.write(f"- hbm_write_bytes_per_launch: {write_b:.0f}\n")
+        fh.write(f"- hbm_bytes_per_launch: {fetch_b + write_b:.0f}\n")
+        fh.write(f"- algorithmic_bytes_per_launch: {algo} (keys once + q + w + score rows "
+                 f"+ T x S scores written; {pairs} visible pairs)\n")
+    print(open(out_md).read())
 
 
 def parse():
@@ -44,6 +146,14 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the CPU oracle baseline (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="after the benchmark, run a 1 GiB copy kernel three times (counter scale)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "OUT_MD"),
+                    help="write the score kernel's traffic summary from two counter runs and exit")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DB", "BENCH_LOG", "OUT_MD"),
+                    help="write the kernel-trace summary of a profiled bench run and exit")
+    ap.add_argument("--commands", default="",
+                    help="text of the commands, for --summarize-pmc / --summarize-trace")
     return ap.parse_args()
 
 
@@ -144,8 +254,42 @@ def cpu_baseline(setup: Setup, budget_s: float):
             "sample": f"{n} random query rows of the chunk (score + top-k, numpy fp64), {dt:.1f} s"}
 
 
+def summarize_trace(db: str, log: str, out_md: str, cmds: str):
+    """Per-kernel dispatch statistics from a rocprofv3 --kernel-trace database,
+    beside the bench line the same run printed."""
+    import sqlite3
+    c = sqlite3.connect(db)
+    rows = c.execute("select name, count(*), avg(duration), min(duration), max(duration), "
+                     "sum(duration) from kernels group by name order by sum(duration) desc").fetchall()
+    line = None
+    with open(log) as fh:
+        for ln in fh:
+            if ln.startswith('{"metric"'):
+                line = json.loads(ln)
+    with open(out_md, "w") as fh:
+        fh.write("# Kernel trace of the hot-path benchmark\n\n")
+        fh.write("Command:\n\n```\n" + cmds.strip() + "\n```\n\n")
+        fh.write("| kernel | calls | avg us | min us | max us | total ms |\n|---|---|---|---|---|---|\n")
+        for name, n, avg, mn, mx, tot in rows:
+            short = name if len(name) < 90 else name[:87] + "..."
+            fh.write(f"| `{short}` | {n} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} | "
+                     f"{tot / 1e6:.2f} |\n")
+        if line:
+            fh.write("\nThe same run's bench line (HIP-event times, ms):\n\n")
+            fh.write(f"- ms: `{json.dumps(line['ms'])}`\n")
+            fh.write(f"- value: {line['value']:.0f} {line['unit']}\n")
+            fh.write(f"- roofline: `{json.dumps(line['roofline'])}`\n")
+    print(open(out_md).read())
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, args.commands)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.workload, args.commands)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the hot path runs on one MI355X and this build "
               "has no multi-GPU path (see the sharding note in the design notes).", file=sys.stderr)
@@ -221,7 +365,8 @@ def main():
         "all_pooled_path": bool(all_pooled),
         "roofline": {"bound": "mfma", "kernel": "indexer_score", "achieved": score_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": score_tflops / PEAK_BF16_TFLOPS, "traffic": None},
+                     "frac": score_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": recorded_traffic(wl.name)},
         "topk_roofline": {"bound": "hbm", "achieved": topk_gbs, "peak": PEAK_HBM_GBS,
                           "unit": "GB/s", "frac": topk_gbs / PEAK_HBM_GBS},
         "attn_roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
@@ -229,6 +374,13 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec))
+    sys.stdout.flush()
+    if args.calibration_copy:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)  # elementwise kernel: reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

@@ -41,9 +41,14 @@
 //     column or query is out of range.
 //   * Four-wave workgroups, two per CU: their barriers are independent, so one
 //     workgroup's epilogue VALU work overlaps the other's MFMAs.
-//   * Grid: workgroups are dealt round-robin to the 8 XCDs; a workgroup's
-//     column split is chosen from blockIdx % 8 so each XCD sweeps one eighth
-//     of the key rows, which then stays resident in that XCD's L2.
+//   * Grid: workgroups are dealt round-robin to the 8 XCDs, and blockIdx % 8
+//     picks the XCD's share: with enough query blocks, XCD x takes query
+//     group x / 4 (every other query block) and column group x % 4 (a quarter
+//     of the key rows, 2 MiB at 128K context, resident in that XCD's 4 MiB
+//     L2), so each query block's q is fetched by 4 XCDs and each key row by
+//     2; with few query blocks every XCD takes all of them and an eighth of
+//     the columns.  Score rows are written non-temporal so the stream of
+//     output does not evict the keys from L2.
 #include <type_traits>
 #include <utility>
 
@@ -84,7 +89,7 @@ __global__ void __launch_bounds__(kThreads, 2)
 indexer_score_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
                      const uint16_t* __restrict__ keys, int64_t rows, int64_t q_pos0, int64_t S,
                      int n_heads, int fold_mask, float* __restrict__ out, int64_t out_stride,
-                     int splits_per_xcd, int64_t cols_per_split) {
+                     int cgroups, int splits_per_cg, int64_t cols_per_split) {
   constexpr int D = KSTEPS * 16;
   constexpr int CPR = D / 8;                 // 16-byte chunks per key row
   constexpr int SWZ = CPR >= 16 ? 15 : CPR - 1;
@@ -104,8 +109,10 @@ indexer_score_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w
   const int g = blockIdx.x;
   const int xcd = g & 7;
   const int r = g >> 3;
-  const int cs = xcd * splits_per_xcd + (r % splits_per_xcd);
-  const int64_t qb = r / splits_per_xcd;
+  const int qgroups = 8 / cgroups;
+  const int cs = (xcd % cgroups) * splits_per_cg + (r % splits_per_cg);
+  const int64_t qb = xcd / cgroups + static_cast<int64_t>(qgroups) * (r / splits_per_cg);
+  if (qb * kQB >= rows) return;  // whole workgroup: no barrier reached yet
   const int64_t col_begin = (int64_t)cs * cols_per_split;
   int64_t col_end = col_begin + cols_per_split;
   if (col_end > S) col_end = S;
@@ -239,7 +246,8 @@ indexer_score_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w
     const float v = col < lane_vis ? tot : -INFINITY;
     const uint32_t off =
         col < rel_end ? lane_row_off + static_cast<uint32_t>(col) * 4u : kDropOffset;
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), orsrc, static_cast<int>(off), 0, 0);
+    // non-temporal (cache policy nt): the output streams past L2
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), orsrc, static_cast<int>(off), 0, 2);
   };
 
   // One 32-column block at LDS byte address tb (first row of the block).
@@ -329,21 +337,25 @@ hipError_t launch_t(const void* q, const float* w, const void* keys, int64_t row
                     int64_t q_pos0, int64_t S, int n_heads, int fold_mask, float* out,
                     int64_t out_stride, hipStream_t s) {
   const int64_t nqb = (rows + kQB - 1) / kQB;
-  // Column splits: a multiple of 8 (one group per XCD), enough workgroups to
-  // fill 256 CUs several times, and at least one tile per split.
-  int64_t per_xcd = (4096 + 8 * nqb - 1) / (8 * nqb);
-  int64_t max_per_xcd = S / (8 * kTileCols);
-  if (max_per_xcd < 1) max_per_xcd = 1;
-  if (per_xcd > max_per_xcd) per_xcd = max_per_xcd;
-  if (per_xcd < 1) per_xcd = 1;
-  const int64_t splits = 8 * per_xcd;
+  // XCD shares: query groups x column groups = 8 (see the kernel comment).
+  const int cgroups = nqb >= 16 ? 4 : 8;
+  const int64_t qgroups = 8 / cgroups;
+  const int64_t nqb_g = (nqb + qgroups - 1) / qgroups;  // query blocks per query group
+  // Column splits per column group: enough workgroups to fill 256 CUs several
+  // times, and at least one tile per split.
+  int64_t per_cg = (4096 + 8 * nqb_g - 1) / (8 * nqb_g);
+  int64_t max_per_cg = S / (static_cast<int64_t>(cgroups) * kTileCols);
+  if (max_per_cg < 1) max_per_cg = 1;
+  if (per_cg > max_per_cg) per_cg = max_per_cg;
+  if (per_cg < 1) per_cg = 1;
+  const int64_t splits = cgroups * per_cg;
   int64_t cps = (S + splits - 1) / splits;
   cps = (cps + kTileCols - 1) / kTileCols * kTileCols;
-  const int64_t grid = splits * nqb;
+  const int64_t grid = 8 * per_cg * nqb_g;
   hipLaunchKernelGGL((indexer_score_kernel<KSTEPS, MT>), dim3(static_cast<unsigned>(grid)),
                      dim3(kThreads), 0, s, static_cast<const uint16_t*>(q), w,
                      static_cast<const uint16_t*>(keys), rows, q_pos0, S, n_heads, fold_mask,
-                     out, out_stride, static_cast<int>(per_xcd), cps);
+                     out, out_stride, cgroups, static_cast<int>(per_cg), cps);
   return hipGetLastError();
 }
 
