@@ -22,8 +22,10 @@
 //     1 KiB row at D = 512), three LDS stages deep: the gathers of tiles i+1
 //     and i+2 are in flight while tile i is computed, and no VGPRs hold
 //     in-flight data;
-//   * 16-byte chunk c of row r sits at slot c ^ (r & 15), which keeps both LDS
-//     read patterns below free of bank conflicts;
+//   * 16-byte chunk c of row r sits at slot c ^ swz(r), swz rotating r's low
+//     4 bits right by one, which keeps both LDS read patterns below free of
+//     bank conflicts; each DMA instruction's row address is wave-uniform
+//     (one lane looks it up per key), so it goes out in the saddr form;
 //   * QK^T is computed transposed, S^T = K . Q^T, with
 //     v_mfma_f32_16x16x32_bf16, each wave over its half of the dims; the two
 //     halves' partial tiles are summed through LDS (a + b == b + a, so both
@@ -56,6 +58,22 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 
+// Reductions over the four 16-lane rows (lanes l, l^16, l^32, l^48) with the
+// row-swap permutes: permlane16_swap of a value with itself pairs rows 0/1 and
+// 2/3, permlane32_swap pairs the two halves; every lane ends with the result.
+__device__ __forceinline__ float xor16_32_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xor16_32_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int D, int NHG, int DSPLIT>
 __global__ void __launch_bounds__(NHG * DSPLIT * 64)
 sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float scale_log2,
@@ -67,6 +85,15 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
   constexpr int DH = D / DSPLIT;          // dims per wave
   constexpr int CPR = D / 8;              // 16-byte chunks per row
   constexpr int SWZ = CPR >= 16 ? 15 : CPR - 1;
+  // LDS slot of 16-byte chunk c of tile row r is c ^ swz(r).  For 16+ chunks
+  // per row swz rotates the row's low 4 bits right by one: still a bijection,
+  // so the QK fragment reads (16 rows, one chunk) stay conflict-free, and the
+  // PV tr16 reads of a 32-lane pass (rows 4m+kb for kb pairs {0,1} / {2,3}, two
+  // adjacent chunks) now cover all 16 bank groups instead of 8 twice.
+  auto swz = [](int r) -> int {
+    if constexpr (SWZ == 15) return ((r & 1) << 3) | ((r >> 1) & 7);
+    else return r & SWZ;
+  };
   constexpr int RPI = 64 / CPR;           // rows per 64-lane load instruction
   constexpr int INSTS = kKeys / RPI;      // load instructions per tile
   constexpr int KSTEP = DH / 32;          // QK^T contraction steps per wave
@@ -76,13 +103,14 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
   // load instructions every wave issues per tile (waves may issue one more)
   constexpr int kNewer = INSTS / NW < 15 ? INSTS / NW : 15;
   __shared__ __attribute__((aligned(16))) uint16_t tiles[kStages][TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) float xs[DSPLIT > 1 ? NW : 1][DSPLIT > 1 ? 64 * 8 : 1];
+  // partial S^T tiles of the two dim halves, double-buffered by tile parity
+  __shared__ __attribute__((aligned(16))) float xs[DSPLIT > 1 ? 2 : 1][DSPLIT > 1 ? NW : 1][DSPLIT > 1 ? 64 * 8 : 1];
   __shared__ int s_last;
   extern __shared__ int s_sel[];  // the query's selection row (topk ints, dynamic)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: SGPR addressing
   const int hg = wave % NHG;   // head group
   const int dh = wave / NHG;   // dim half
   const int kb = lane >> 4;    // 16-lane group
@@ -128,15 +156,33 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
   };
 
   // Gather tile `tile` into stage `buf`: instruction i moves rows
-  // i*RPI .. i*RPI+RPI-1, lane -> (row, slot).
-  auto issue_tile = [&](int tile, int buf) {
-    for (int i = wave; i < INSTS; i += NW) {
-      const int row = i * RPI + lane / CPR;
-      const int slot = lane % CPR;
-      const uint16_t* rp = key_row(tile * kKeys + row);
-      if (!rp) rp = self_row;
-      global_to_lds16(rp + (slot ^ (row & SWZ)) * 8, &tiles[buf][i * RPI * D]);
+  // i*RPI .. i*RPI+RPI-1, lane -> (row, slot).  Returns the tile's validity
+  // mask (bit k: key slot k has a row).  With one row per instruction, lane k
+  // looks up key k's row once and each instruction takes its row address from
+  // the owning lane (a wave-uniform base plus per-lane chunk offsets).
+  auto issue_tile = [&](int tile, int buf) -> uint32_t {
+    const uint16_t* rk = lane < kKeys ? key_row(tile * kKeys + lane) : nullptr;
+    const uint32_t valid = static_cast<uint32_t>(__ballot(rk != nullptr));
+    if constexpr (RPI == 1) {
+      const uint64_t ra = reinterpret_cast<uint64_t>(rk ? rk : self_row);
+      const uint32_t ra_lo = static_cast<uint32_t>(ra), ra_hi = static_cast<uint32_t>(ra >> 32);
+      for (int i = wave; i < INSTS; i += NW) {
+        const uint64_t base =
+            (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ra_hi), i))) << 32) |
+            static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ra_lo), i));
+        const uint32_t off = static_cast<uint32_t>(((lane % CPR) ^ swz(i)) * 16);
+        global_to_lds16_s(reinterpret_cast<const void*>(base), off, &tiles[buf][i * D]);
+      }
+    } else {
+      for (int i = wave; i < INSTS; i += NW) {
+        const int row = i * RPI + lane / CPR;
+        const int slot = lane % CPR;
+        const uint16_t* rp = key_row(tile * kKeys + row);
+        if (!rp) rp = self_row;
+        global_to_lds16(rp + (slot ^ swz(row)) * 8, &tiles[buf][i * RPI * D]);
+      }
     }
+    return valid;
   };
 
   // ---- Q block (B operand of S^T = K.Q^T): lane group kb holds dims
@@ -170,63 +216,117 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
   const int trow1 = 16 + trow0;           // mt = 1
   const int dsub = 4 * (l16 & 3);
 
-  issue_tile(0, 0);
-  if (n_tiles > 1) issue_tile(1, 1);
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile % kStages;
-    // wait for this wave's loads of `tile`; the loads of tile+1 (issued later,
-    // at least kNewer instructions per wave) may stay in flight
-    if (tile + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0F70 | kNewer);
-    else __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    // publishes `tile` and retires tile-1: its stage takes tile+2
-    __syncthreads();
-    if (tile + 2 < n_tiles) issue_tile(tile + 2, (tile + 2) % kStages);
-    const uint16_t* tb = tiles[buf];
-
-    // ---- validity of the tile's 32 key slots as a wave-uniform bit mask
-    const uint32_t vmask = static_cast<uint32_t>(
-        __ballot(lane < kKeys && key_row(tile * kKeys + lane) != nullptr));
-
-    // ---- partial S^T (32 keys x 16 heads) over this wave's dims.  Fragment
-    // reads go out in batches; scheduling barriers keep batch b+1's reads
-    // issued ahead of batch b's MFMAs so LDS latency is paid once per batch.
-    f32x4_t sacc0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, sacc1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    {
-      constexpr int QB = KSTEP < 4 ? KSTEP : 4;  // k-steps per batch
-      const uint16_t* rb0 = tb + qk_row0 * D;
-      const uint16_t* rb1 = tb + qk_row1 * D;
-      bf16x8_t fa[2][2][QB];  // [buffer][m tile][step]
-      auto load_batch = [&](int j0, int bi) {
+  // ---- partial S^T (32 keys x 16 heads) of tile `tile` over this wave's
+  // dims.  Fragment reads go out in batches; scheduling barriers keep batch
+  // b+1's reads issued ahead of batch b's MFMAs.
+  auto qk = [&](int tile, f32x4_t& sacc0, f32x4_t& sacc1) {
+    const uint16_t* tb = tiles[tile % kStages];
+    sacc0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    sacc1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    constexpr int QB = KSTEP < 4 ? KSTEP : 4;  // k-steps per batch
+    const uint16_t* rb0 = tb + qk_row0 * D;
+    const uint16_t* rb1 = tb + qk_row1 * D;
+    bf16x8_t fa[2][2][QB];  // [buffer][m tile][step]
+    auto load_batch = [&](int j0, int bi) {
 #pragma unroll
-        for (int u = 0; u < QB; ++u) {
-          const int chunk = dh * (DH / 8) + kb * KSTEP + j0 + u;
-          fa[bi][0][u] = *reinterpret_cast<const bf16x8_t*>(rb0 + ((chunk ^ (qk_row0 & SWZ)) * 8));
-          fa[bi][1][u] = *reinterpret_cast<const bf16x8_t*>(rb1 + ((chunk ^ (qk_row1 & SWZ)) * 8));
-        }
-      };
-      load_batch(0, 0);
-#pragma unroll
-      for (int j0 = 0; j0 < KSTEP; j0 += QB) {
-        const int bi = (j0 / QB) & 1;
-        __builtin_amdgcn_sched_barrier(0);
-        if (j0 + QB < KSTEP) load_batch(j0 + QB, bi ^ 1);
-#pragma unroll
-        for (int u = 0; u < QB; ++u) {
-          sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[bi][0][u], qf[j0 + u], sacc0, 0, 0, 0);
-          sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[bi][1][u], qf[j0 + u], sacc1, 0, 0, 0);
-        }
+      for (int u = 0; u < QB; ++u) {
+        const int chunk = dh * (DH / 8) + kb * KSTEP + j0 + u;
+        fa[bi][0][u] = *reinterpret_cast<const bf16x8_t*>(rb0 + ((chunk ^ swz(qk_row0)) * 8));
+        fa[bi][1][u] = *reinterpret_cast<const bf16x8_t*>(rb1 + ((chunk ^ swz(qk_row1)) * 8));
       }
-      __builtin_amdgcn_sched_barrier(0);
+    };
+    load_batch(0, 0);
+#pragma unroll
+    for (int j0 = 0; j0 < KSTEP; j0 += QB) {
+      const int bi = (j0 / QB) & 1;
+      if (j0 + QB < KSTEP) load_batch(j0 + QB, bi ^ 1);
+#pragma unroll
+      for (int u = 0; u < QB; ++u) {
+        sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[bi][0][u], qf[j0 + u], sacc0, 0, 0, 0);
+        sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[bi][1][u], qf[j0 + u], sacc1, 0, 0, 0);
+      }
     }
+  };
+  // two planes of 64 x 16 B: each 16-lane phase covers all 64 banks once
+  auto put_partial = [&](int tile, const f32x4_t& sacc0, const f32x4_t& sacc1) {
     if constexpr (DSPLIT > 1) {
-      // sum with the partner wave (same heads, other dims)
-      *reinterpret_cast<f32x4_t*>(&xs[wave][lane * 8]) = sacc0;
-      *reinterpret_cast<f32x4_t*>(&xs[wave][lane * 8 + 4]) = sacc1;
-      __syncthreads();
-      const int partner = (wave + NHG) % NW;
-      sacc0 += *reinterpret_cast<const f32x4_t*>(&xs[partner][lane * 8]);
-      sacc1 += *reinterpret_cast<const f32x4_t*>(&xs[partner][lane * 8 + 4]);
+      *reinterpret_cast<f32x4_t*>(&xs[tile & 1][wave][lane * 4]) = sacc0;
+      *reinterpret_cast<f32x4_t*>(&xs[tile & 1][wave][256 + lane * 4]) = sacc1;
     }
+  };
+  auto add_partner = [&](int tile, f32x4_t& sacc0, f32x4_t& sacc1) {
+    if constexpr (DSPLIT > 1) {
+      // same heads, other dims (a + b == b + a: both waves hold identical scores)
+      const int partner = (wave + NHG) % NW;
+      sacc0 += *reinterpret_cast<const f32x4_t*>(&xs[tile & 1][partner][lane * 4]);
+      sacc1 += *reinterpret_cast<const f32x4_t*>(&xs[tile & 1][partner][256 + lane * 4]);
+    }
+  };
+  // ---- O += P . V over this wave's dims; P = A operand (head l16, keys
+  // mt*16 + 4*i + kb); V via tr16: lane j of a 16-lane block addresses key
+  // q = j/4 of the 4 and dims 4*(j%4) .. +3 of the 16-dim column tile
+  auto pv = [&](int tile, const bf16x8_t& pa) {
+    const uint16_t* tb = tiles[tile % kStages];
+    constexpr int PB = NTILE < 4 ? NTILE : 4;  // column tiles per batch
+    const uint16_t* r0 = tb + trow0 * D;
+    const uint16_t* r1 = tb + trow1 * D;
+    const int sw0 = swz(trow0), sw1 = swz(trow1);
+    i16x4_t fv[2][2][PB];  // [buffer][key group][column tile]
+    auto load_batch = [&](int n0, int bi) {
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        const int d = dh * DH + (n0 + u) * 16 + dsub;
+        const int ch = d >> 3;
+        const int off = d & 7;
+        fv[bi][0][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(r0 + ((ch ^ sw0) * 8) + off));
+        fv[bi][1][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(r1 + ((ch ^ sw1) * 8) + off));
+      }
+    };
+    load_batch(0, 0);
+#pragma unroll
+    for (int n0 = 0; n0 < NTILE; n0 += PB) {
+      const int bi = (n0 / PB) & 1;
+      __builtin_amdgcn_sched_barrier(0);
+      if (n0 + PB < NTILE) load_batch(n0 + PB, bi ^ 1);
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        bf16x8_t b;
+        *reinterpret_cast<i16x4_t*>(&b) = fv[bi][0][u];
+        *(reinterpret_cast<i16x4_t*>(&b) + 1) = fv[bi][1][u];
+        o[n0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, b, o[n0 + u], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Software pipeline, one workgroup barrier per tile.  Iteration `tile`
+  // finishes that tile (its partner partial, softmax, P.V) while computing
+  // the next tile's partial S^T, so the MFMAs of QK(tile+1) run beside the
+  // softmax VALU work.  Stage use at iteration `tile`: tile (P.V), tile+1
+  // (QK), tile+2 (gather in flight, into the stage tile-1 released).
+  // Validity masks of the tiles in flight: current, next, and the one after.
+  uint32_t vm_cur = issue_tile(0, 0);
+  uint32_t vm_next = n_tiles > 1 ? issue_tile(1, 1) : 0u;
+  f32x4_t s_own0, s_own1;  // this wave's partial S^T of the current tile
+  if (n_tiles > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | kNewer);  // tile 0 landed; tile 1 may fly
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();  // publishes tile 0
+  qk(0, s_own0, s_own1);
+  put_partial(0, s_own0, s_own1);
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's gather of tile+1 (issued last) landed
+    // publishes the partials of `tile` and the rows of tile+1; every wave
+    // is done with tile-1, whose stage takes tile+2
+    __syncthreads();
+    const uint32_t vm_after = tile + 2 < n_tiles ? issue_tile(tile + 2, (tile + 2) % kStages) : 0u;
+    const uint32_t vmask = vm_cur;
+    vm_cur = vm_next;
+    vm_next = vm_after;
+
+    f32x4_t sacc0 = s_own0, sacc1 = s_own1;
+    add_partner(tile, sacc0, sacc1);
+    // the next tile's partial S^T: its MFMAs overlap the softmax below
+    if (tile + 1 < n_tiles) qk(tile + 1, s_own0, s_own1);
 
     // lane holds, for head l16, keys mt*16 + 4*i + kb (output rows 4*kb + i)
     float sv[8];
@@ -238,40 +338,21 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
       sv[4 + i] = ((vmask >> k1) & 1u) ? sacc1[i] * scale_log2 : -INFINITY;
       mx = fmaxf(mx, fmaxf(sv[i], sv[4 + i]));
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor16_32_max(mx);
     // Lazy rescale: exponentials are taken against a reference max m_ref that
     // only moves when the running max passes it by more than kSlack (log2
     // units); p <= 2^kSlack stays far from fp32 / bf16 overflow.
     const bool bump = mx > m_ref + kSlack;
-    if (__ballot(bump)) {
-      const float m_new = bump ? mx : m_ref;
-      const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
-      l_run *= alpha;
-      m_ref = m_new;
-      float al[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kb + i);
-#pragma unroll
-      for (int n = 0; n < NTILE; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[n][i] *= al[i];
-    }
-    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    const float m_new = bump ? mx : m_ref;
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     float psum = 0.f;
     float pr[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      pr[i] = exp2f(sv[i] - m_use);
+      pr[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);  // v_exp_f32 (tiny results flush to 0)
       psum += pr[i];
     }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    l_run += psum;
-
-    // ---- O += P . V over this wave's dims; P = A operand (head l16, keys
-    // mt*16 + 4*i + kb); V via tr16: lane j of a 16-lane block addresses key
-    // q = j/4 of the 4 and dims 4*(j%4) .. +3 of the 16-dim column tile
+    psum = xor16_32_sum(psum);
     bf16x8_t pa;
     {
       uint32_t pk[4];
@@ -281,38 +362,21 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
       pk[3] = pack_bf16x2(pr[6], pr[7]);
       pa = *reinterpret_cast<const bf16x8_t*>(pk);
     }
-    {
-      constexpr int PB = NTILE < 4 ? NTILE : 4;  // column tiles per batch
-      const uint16_t* r0 = tb + trow0 * D;
-      const uint16_t* r1 = tb + trow1 * D;
-      const int sw0 = trow0 & SWZ, sw1 = trow1 & SWZ;
-      i16x4_t fv[2][2][PB];  // [buffer][key group][column tile]
-      auto load_batch = [&](int n0, int bi) {
+    if (tile + 1 < n_tiles) put_partial(tile + 1, s_own0, s_own1);
+    if (__ballot(bump)) {
+      const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
+      l_run *= alpha;
+      float al[4];
 #pragma unroll
-        for (int u = 0; u < PB; ++u) {
-          const int d = dh * DH + (n0 + u) * 16 + dsub;
-          const int ch = d >> 3;
-          const int off = d & 7;
-          fv[bi][0][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(r0 + ((ch ^ sw0) * 8) + off));
-          fv[bi][1][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(r1 + ((ch ^ sw1) * 8) + off));
-        }
-      };
-      load_batch(0, 0);
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kb + i);
 #pragma unroll
-      for (int n0 = 0; n0 < NTILE; n0 += PB) {
-        const int bi = (n0 / PB) & 1;
-        __builtin_amdgcn_sched_barrier(0);
-        if (n0 + PB < NTILE) load_batch(n0 + PB, bi ^ 1);
+      for (int n = 0; n < NTILE; ++n)
 #pragma unroll
-        for (int u = 0; u < PB; ++u) {
-          bf16x8_t b;
-          *reinterpret_cast<i16x4_t*>(&b) = fv[bi][0][u];
-          *(reinterpret_cast<i16x4_t*>(&b) + 1) = fv[bi][1][u];
-          o[n0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, b, o[n0 + u], 0, 0, 0);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 4; ++i) o[n][i] *= al[i];
     }
+    m_ref = m_new;
+    l_run += psum;
+    pv(tile, pa);
   }
   __syncthreads();  // every wave is done with the tile stages
 
