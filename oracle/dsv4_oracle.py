@@ -64,14 +64,17 @@ class PoolingCacheState:
     """Host model of one compressor's PoolingCache.
 
     Holds the pooled rows appended so far (``rows[:n_rows]``), and the raw
-    tokens not yet pooled (``rem``, fewer than ``RATIO`` of them).  Pooled rows
-    are appended in place at offset ``n_rows`` [P2 commit 4].
+    tokens not yet pooled (``rem``, fewer than ``ratio`` of them).  Pooled rows
+    are appended in place at offset ``n_rows`` [P2 commit 4].  ``ratio`` is 4
+    on the indexer's path; the sibling CompressedAttention mode pools 128 rows
+    [P2 commit 1 and the rebase note: ratio-128 prefill].
     """
 
-    def __init__(self, dim: int, capacity: int, out_bf16: bool = True):
+    def __init__(self, dim: int, capacity: int, out_bf16: bool = True, ratio: int = RATIO):
         self.dim = dim
         self.capacity = capacity
         self.out_bf16 = out_bf16
+        self.ratio = ratio
         self.rows = np.zeros((capacity, dim), dtype=np.float32)
         self.n_rows = 0
         self.rem = np.zeros((0, dim), dtype=np.float32)
@@ -83,11 +86,11 @@ class PoolingCacheState:
     @property
     def tokens_consumed(self) -> int:
         # Reading: groups are aligned to absolute position 0, so the stream
-        # position of the next raw token is RATIO * n_rows + n_rem.
-        return RATIO * self.n_rows + self.n_rem
+        # position of the next raw token is ratio * n_rows + n_rem.
+        return self.ratio * self.n_rows + self.n_rem
 
     def copy(self) -> "PoolingCacheState":
-        c = PoolingCacheState(self.dim, self.capacity, self.out_bf16)
+        c = PoolingCacheState(self.dim, self.capacity, self.out_bf16, self.ratio)
         c.rows = self.rows.copy()
         c.n_rows = self.n_rows
         c.rem = self.rem.copy()
@@ -95,42 +98,44 @@ class PoolingCacheState:
 
 
 def pool_group(tokens_f32: np.ndarray, out_bf16: bool) -> np.ndarray:
-    """One pooled row from RATIO consecutive raw rows.
+    """One pooled row from ``r`` consecutive raw rows (r = the ratio, 4 or 128).
 
     Reading (pages name a ratio-4 "pooling" but give no formula): mean pool.
-    The sum is taken in float32, strictly left to right, ((a+b)+c)+d, each add
-    rounded to float32, then multiplied by 0.25 (exact) and rounded to the
-    storage type (bfloat16, ties to even).  No fused multiply-add.
+    The sum is taken in float32, strictly left to right, ((a+b)+c)+d..., each
+    add rounded to float32, then multiplied by 1/r (exact for a power of two)
+    and rounded to the storage type (bfloat16, ties to even).  No fused
+    multiply-add.  The same reading serves the ratio-128 pool.
     """
-    assert tokens_f32.shape[0] == RATIO
+    r = tokens_f32.shape[0]
     t = tokens_f32.astype(np.float32)
     acc = t[0].copy()
-    for i in range(1, RATIO):
+    for i in range(1, r):
         acc = (acc + t[i]).astype(np.float32)  # one float32 rounding per add
-    mean = (acc * np.float32(1.0 / RATIO)).astype(np.float32)
+    mean = (acc * np.float32(1.0 / r)).astype(np.float32)
     return round_to_bf16(mean) if out_bf16 else mean
 
 
 def compress(state: PoolingCacheState, x) -> int:
-    """Feed ``x`` ([n_new, dim] raw rows) through the ratio-4 compressor.
+    """Feed ``x`` ([n_new, dim] raw rows) through the state's compressor.
 
-    [P1 Correctness]: a non-aligned prefill of 10 tokens yields two pooled
-    rows and a two-token remainder; the remainder is carried into the next
-    call.  The concatenation (old remainder, new rows) is cut into groups of
-    RATIO; each whole group becomes one pooled row appended at ``n_rows``
+    [P1 Correctness]: a non-aligned ratio-4 prefill of 10 tokens yields two
+    pooled rows and a two-token remainder; the remainder is carried into the
+    next call.  The concatenation (old remainder, new rows) is cut into groups
+    of ``ratio``; each whole group becomes one pooled row appended at ``n_rows``
     [P2 commit 4]; what is left becomes the new remainder.
     Returns the number of rows appended.  Raises ValueError when the append
     would pass ``capacity`` (state unchanged).
     """
     x = np.asarray(x, dtype=np.float32).reshape(-1, state.dim)
     cat = np.concatenate([state.rem, x], axis=0)
-    groups = cat.shape[0] // RATIO
+    r = state.ratio
+    groups = cat.shape[0] // r
     if state.n_rows + groups > state.capacity:
         raise ValueError("pooled rows would exceed capacity")
     for j in range(groups):
-        state.rows[state.n_rows + j] = pool_group(cat[RATIO * j: RATIO * j + RATIO], state.out_bf16)
+        state.rows[state.n_rows + j] = pool_group(cat[r * j: r * j + r], state.out_bf16)
     state.n_rows += groups
-    state.rem = cat[RATIO * groups:].copy()
+    state.rem = cat[r * groups:].copy()
     return groups
 
 
@@ -138,16 +143,16 @@ def compress(state: PoolingCacheState, x) -> int:
 # Pooled-row visibility  [P2 commit 1 and commit 5]
 # --------------------------------------------------------------------------
 
-def visible_rows(p: int) -> int:
+def visible_rows(p: int, ratio: int = RATIO) -> int:
     """Number of pooled rows a query at absolute position ``p`` may see.
 
     [P2 commit 1] rebuilds pooled visibility from offsets; [P2 commit 5]
-    names it the pooled-ratio causal mask.  Reading: pooled row s summarises
-    tokens RATIO*s .. RATIO*s+RATIO-1, and is visible to position p once all of
-    them are at or before p, i.e. RATIO*(s+1) <= p+1.  Counting those s gives
-    floor((p+1)/RATIO).
+    names it the pooled-ratio causal mask.  Reading: with ratio r, pooled row
+    s summarises tokens r*s .. r*s+r-1, and is visible to position p once all
+    of them are at or before p, i.e. r*(s+1) <= p+1.  Counting those s gives
+    floor((p+1)/r).
     """
-    return (p + 1) // RATIO
+    return (p + 1) // ratio
 
 
 # --------------------------------------------------------------------------
@@ -283,7 +288,7 @@ def indexer_select(q, w, K, n_attn_rows: int, T: int, q_pos0: int, topk: int, S:
 # --------------------------------------------------------------------------
 
 def sparse_prefill_attention(q, q_pos0: int, raw_kv, raw_pos0: int, window: int,
-                             pooled, sel_idx, scale: float) -> np.ndarray:
+                             pooled, sel_idx, scale: float, ratio: int = RATIO) -> np.ndarray:
     """Windowed + pooled attention for T queries, fp64.
 
     [P2 commit 1]: one attention over the sliding raw-token window plus the
@@ -292,22 +297,27 @@ def sparse_prefill_attention(q, q_pos0: int, raw_kv, raw_pos0: int, window: int,
     rebuilt from offsets.
 
     q: [T, H, D]; raw_kv: [n_raw, D] raw rows for positions raw_pos0.. ;
-    pooled: [>=S, D] pooled rows; sel_idx: [T, k] int (-1 = empty slot) or
-    None for "every visible pooled row".  Readings: keys and values are the
-    same rows shared by all heads; the window holds positions p-window+1 .. p
-    (clipped at 0); a pooled row is a key distinct from the raw rows (both
-    are attended); no sink, no extra bias; softmax in fp64.
+    pooled: [>=S, D] pooled rows, or None for the window-only mode (the
+    LocalAttention sibling of [P2 commit 1]: no pooled keys at all); sel_idx:
+    [T, k] int (-1 = empty slot) or None for "every visible pooled row" (the
+    CompressedAttention sibling, ratio 128, and the small-pool path).
+    ``ratio`` is the pool's ratio, used for pooled visibility.  Readings: keys
+    and values are the same rows shared by all heads; the window holds
+    positions p-window+1 .. p (clipped at 0); a pooled row is a key distinct
+    from the raw rows (both are attended); no sink, no extra bias; softmax in
+    fp64.
     """
     q = np.asarray(q, dtype=np.float64)
     raw = np.asarray(raw_kv, dtype=np.float64)
-    pooled = np.asarray(pooled, dtype=np.float64)
+    if pooled is not None:
+        pooled = np.asarray(pooled, dtype=np.float64)
     T, H, D = q.shape
     out = np.zeros((T, H, D), dtype=np.float64)
     for t in range(T):
         p = q_pos0 + t
         lo = max(0, p - window + 1)
         keys = [raw[j - raw_pos0] for j in range(lo, p + 1)]
-        vis = visible_rows(p)
+        vis = 0 if pooled is None else visible_rows(p, ratio)
         if sel_idx is None:
             chosen = list(range(vis))
         else:

@@ -132,6 +132,64 @@ def test_pool_capacity_overflow_leaves_state():
     np.testing.assert_array_equal(st.rem, before[1])
 
 
+# ------------------------------------------- ratio-128 pool (CompressedAttention)
+
+def test_pool_ratio128_constant_and_ramp_closed_forms():
+    st = O.PoolingCacheState(dim=3, capacity=4, ratio=128)
+    O.compress(st, np.full((300, 3), 0.75, dtype=np.float32))
+    assert st.n_rows == 2 and st.n_rem == 300 - 256
+    assert np.all(st.rows[:2] == np.float32(0.75))
+    # x_p = p: row s = mean(128s .. 128s+127) = 128s + 63.5.  Every partial sum
+    # is an integer below 2^24, so the float32 result is exact; stored in
+    # float32 it is the closed form, stored in bf16 it is that value rounded
+    # by torch's own conversion.
+    n = 128 * 5
+    x = np.repeat(np.arange(n, dtype=np.float32)[:, None], 2, axis=1)
+    want = 128 * np.arange(5) + 63.5
+    st = O.PoolingCacheState(dim=2, capacity=5, out_bf16=False, ratio=128)
+    O.compress(st, x)
+    np.testing.assert_array_equal(st.rows[:, 1], want)
+    st = O.PoolingCacheState(dim=2, capacity=5, out_bf16=True, ratio=128)
+    O.compress(st, x)
+    np.testing.assert_array_equal(
+        st.rows[:, 0], torch.tensor(want, dtype=torch.float32).to(torch.bfloat16).float().numpy())
+
+
+def test_pool_ratio128_order_left_to_right():
+    # 1 followed by 127 copies of 2^-24: each add is a tie that rounds back to
+    # 1, so the left-to-right float32 sum is exactly 1 and the mean 2^-7.  Any
+    # pairwise or blocked order would collect the small terms first and land
+    # above 1.
+    x = np.full((128, 1), 2.0 ** -24, dtype=np.float32)
+    x[0, 0] = 1.0
+    st = O.PoolingCacheState(dim=1, capacity=1, out_bf16=False, ratio=128)
+    O.compress(st, x)
+    assert st.rows[0, 0] == np.float32(2.0 ** -7)
+    assert float(np.sum(x.astype(np.float64))) / 128 > 2.0 ** -7
+
+
+def test_pool_ratio128_chunk_split_invariance():
+    rng = np.random.default_rng(71)
+    n = 128 * 3 + 17
+    x = rng.standard_normal((n, 4)).astype(np.float32)
+    ref = O.PoolingCacheState(dim=4, capacity=3, ratio=128)
+    O.compress(ref, x)
+    assert ref.n_rows == 3 and ref.n_rem == 17
+    rs = np.random.default_rng(5)
+    for _ in range(12):
+        cuts = np.sort(rs.integers(0, n + 1, size=rs.integers(1, 6)))
+        st = O.PoolingCacheState(dim=4, capacity=3, ratio=128)
+        pos = 0
+        for m in np.diff(np.concatenate([[0], cuts, [n]])):
+            O.compress(st, x[pos:pos + m])
+            pos += m
+        np.testing.assert_array_equal(st.rows, ref.rows)
+        np.testing.assert_array_equal(st.rem, ref.rem)
+    # the mean of a group is the float64 mean to within float32 summation error
+    g = x[:128].astype(np.float64).mean(axis=0)
+    np.testing.assert_allclose(ref.rows[0], g, atol=2e-2)
+
+
 # ---------------------------------------------------------------- visibility
 
 def test_visibility_against_token_enumeration():
@@ -148,6 +206,14 @@ def test_visibility_against_token_enumeration():
                 break
         assert O.visible_rows(p) == brute
     assert O.visible_rows(2) == 0 and O.visible_rows(3) == 1
+
+
+@pytest.mark.parametrize("ratio", [2, 128])
+def test_visibility_other_ratios_against_enumeration(ratio):
+    for p in range(0, 3 * ratio + 5):
+        brute = sum(1 for s in range(p + 2) if ratio * s + ratio - 1 <= p)
+        assert O.visible_rows(p, ratio) == brute
+    assert O.visible_rows(ratio - 2, ratio) == 0 and O.visible_rows(ratio - 1, ratio) == 1
 
 
 def test_visible_pairs_closed_form():
@@ -426,3 +492,58 @@ def test_attention_null_selection_and_trimmed_raw_buffer():
     r0 = q_pos0 - W + 1
     c = O.sparse_prefill_attention(q, q_pos0, raw_full[r0:], r0, W, pooled, None, 0.4)
     np.testing.assert_array_equal(a, c)
+
+
+def _masked_sdpa(q, keys, mask, scale):
+    H = q.shape[1]
+    KK = np.broadcast_to(keys, (H,) + keys.shape).copy()
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.transpose(1, 0, 2)), torch.from_numpy(KK), torch.from_numpy(KK),
+        attn_mask=torch.from_numpy(mask), scale=scale).numpy().transpose(1, 0, 2)
+
+
+def test_local_attention_is_banded_causal_sdpa():
+    # Window-only mode (no pooled keys): sliding-window causal attention.
+    rng = np.random.default_rng(18)
+    T, H, D, W, q_pos0 = 9, 3, 8, 4, 11
+    q = rng.standard_normal((T, H, D))
+    raw_pos0 = 2
+    raw = rng.standard_normal((q_pos0 + T - raw_pos0, D))
+    got = O.sparse_prefill_attention(q, q_pos0, raw, raw_pos0, W, None, None, 0.35)
+    mask = np.zeros((T, raw.shape[0]), dtype=bool)
+    for t in range(T):
+        p = q_pos0 + t
+        for j in range(raw.shape[0]):
+            mask[t, j] = p - W < raw_pos0 + j <= p
+    np.testing.assert_allclose(got, _masked_sdpa(q, raw, mask, 0.35), rtol=1e-10, atol=1e-12)
+    # a pool of any size is ignored when it is passed as None, and an
+    # all-empty selection over a real pool gives the same result
+    S = (q_pos0 + T) // 4
+    pooled = rng.standard_normal((S, D))
+    empty = np.full((T, 3), -1, dtype=np.int32)
+    same = O.sparse_prefill_attention(q, q_pos0, raw, raw_pos0, W, pooled, empty, 0.35)
+    np.testing.assert_array_equal(got, same)
+
+
+def test_compressed_attention_ratio128_matches_masked_sdpa():
+    # CompressedAttention: every pooled row whose 128 tokens are all at or
+    # before the query is attended, together with the raw window.
+    rng = np.random.default_rng(19)
+    T, H, D, W = 6, 2, 4, 5
+    q_pos0 = 128 * 3 - 3      # queries straddle the boundary 383 -> 384
+    raw_pos0 = q_pos0 - W + 1
+    raw = rng.standard_normal((T + W - 1, D))
+    S = (q_pos0 + T) // 128
+    pooled = rng.standard_normal((S, D))
+    got = O.sparse_prefill_attention(q := rng.standard_normal((T, H, D)), q_pos0, raw,
+                                     raw_pos0, W, pooled, None, 0.3, ratio=128)
+    keys = np.concatenate([raw, pooled], axis=0)
+    mask = np.zeros((T, keys.shape[0]), dtype=bool)
+    for t in range(T):
+        p = q_pos0 + t
+        for j in range(raw.shape[0]):
+            mask[t, j] = p - W < raw_pos0 + j <= p
+        for s_ in range(S):
+            mask[t, raw.shape[0] + s_] = 128 * s_ + 127 <= p
+    assert mask[:, raw.shape[0]:].sum(axis=1).tolist() == [2, 2, 3, 3, 3, 3]
+    np.testing.assert_allclose(got, _masked_sdpa(q, keys, mask, 0.3), rtol=1e-10, atol=1e-12)
