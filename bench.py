@@ -146,6 +146,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the CPU oracle baseline (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-modes", action="store_true",
+                    help="skip the local / ratio-128 attention mode measurements")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after the benchmark, run a 1 GiB copy kernel three times (counter scale)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "OUT_MD"),
@@ -223,6 +225,44 @@ def timed_kernel(fn, reps: int) -> float:
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / reps
+
+
+def measure_modes(setup: Setup, reps: int) -> dict:
+    """The sibling attention modes of the same fused kernel on this chunk:
+    window-only (LocalAttention) and window + every visible ratio-128 pooled
+    row (CompressedAttention, after the chunk's ratio-128 compress).  Each is
+    timed with HIP events over `reps` launches; FLOPs are 4*H*D per (query,
+    key) and the gather is one head_dim row of bf16 per (query, key)."""
+    d, wl = setup.dsv4, setup.wl
+    T, H, D, W = wl.chunk, wl.heads, wl.head_dim, wl.window
+    rows_t, _ = SI.prefix_rows_ratio(wl, 0, 128)
+    n128 = rows_t.shape[0]
+    c128 = d.PoolCache(n128 + T // 128 + 1, D, ratio=128)
+    c128.rows[:n128].copy_(rows_t)
+
+    def comp128():
+        c128.set_state(n128, 0)
+        d.dsv4_compress(c128, setup.chunk_kv)
+
+    ms_c128 = timed_kernel(comp128, reps)
+    comp128()
+    out = setup.out
+    ms_local = timed_kernel(lambda: d.dsv4_sparse_prefill_attn(
+        setup.q_attn, wl.q_pos0, setup.raw_kv, setup.raw_pos0, W, None, None, out), reps)
+    ms_comp = timed_kernel(lambda: d.dsv4_sparse_prefill_attn(
+        setup.q_attn, wl.q_pos0, setup.raw_kv, setup.raw_pos0, W, c128, None, out), reps)
+    res = {}
+    for name, ms, pooled in (("local_attention", ms_local, lambda p: 0),
+                             ("compressed_attention_r128", ms_comp, lambda p: (p + 1) // 128)):
+        keys = sum(min(W, p + 1) + pooled(p) for p in range(wl.q_pos0, wl.q_pos0 + T))
+        tflops = 4 * H * D * keys / (ms * 1e-3) / 1e12
+        gbs = keys * D * 2 / (ms * 1e-3) / 1e9
+        res[name] = {"ms": ms, "query_rows_per_s": T / (ms * 1e-3), "keys_per_query": keys / T,
+                     "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS},
+                     "gather_GBps": gbs}
+    res["compress_r128_ms"] = ms_c128
+    return res
 
 
 def cpu_baseline(setup: Setup, budget_s: float):
@@ -340,6 +380,7 @@ def main():
                      for p in range(wl.q_pos0, wl.q_pos0 + T))
     attn_tflops = attn_flops / (attn * 1e-3) / 1e12
 
+    modes = measure_modes(setup, max(5, args.steps // 2)) if not args.no_modes else None
     cpu = cpu_baseline(setup, args.cpu_seconds) if args.cpu_seconds > 0 else None
     rec = {
         "metric": "indexer score+top-k query rows/s and pooled-row scores/s at 128K ctx; MFMA util",
@@ -371,6 +412,7 @@ def main():
                           "unit": "GB/s", "frac": topk_gbs / PEAK_HBM_GBS},
         "attn_roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                           "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS},
+        "modes": modes,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec))

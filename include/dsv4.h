@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define DSV4_ABI_VERSION 1
+#define DSV4_ABI_VERSION 2
 
 /* Return codes. */
 #define DSV4_OK                0
@@ -62,6 +62,7 @@ extern "C" {
 #define DSV4_MAX_TOPK        4096
 #define DSV4_MAX_INDEX_HEADS 64
 #define DSV4_MAX_HEADS       64
+#define DSV4_MAX_RATIO       256
 
 /*
  * PoolingCache of one compressor [P1 Summary, Correctness; P2 commit 4].
@@ -69,7 +70,11 @@ extern "C" {
  * rem  : device [ratio-1][dim] raw rows received but not yet pooled;
  *        rows [0, n_rem) are valid.
  * The stream position of the next raw token is ratio*n_rows + n_rem.
- * dsv4_compress updates n_rows and n_rem on success.  ratio must be 4.
+ * dsv4_compress updates n_rows and n_rem on success.
+ * ratio: 4 for the indexer path and sparse attention, 128 for the
+ * CompressedAttention mode [P2 commit 1; the ratio-128 prefill route it
+ * builds on]; 2 <= ratio <= DSV4_MAX_RATIO is accepted by dsv4_compress and
+ * dsv4_sparse_prefill_attn, the indexer entry points require ratio 4.
  * dtype DSV4_BF16 is the hot-path type; DSV4_F32 is accepted by
  * dsv4_compress only.
  */
@@ -111,15 +116,18 @@ int64_t dsv4_score_stride(int64_t n_rows);
 int dsv4_indexer_scratch_bytes(int64_t tile_rows, int64_t max_rows, size_t* bytes);
 
 /*
- * Ratio-4 compressor [P1 Correctness; P2 commit 4].
+ * Pooling compressor, r = cache->ratio [P1 Correctness (ratio 4); P2 commit
+ * 4].
  * x     : device [n_new][cache->dim] raw rows in cache->dtype (may be NULL
  *         iff n_new == 0).
- * The old remainder followed by x is cut into groups of 4 consecutive rows;
- * each whole group becomes one pooled row (mean of the 4 rows: float32 sum
- * taken left to right, times 0.25, rounded to the storage type, ties to
- * even), appended in place at cache->n_rows; the rows left over become the
- * new remainder.  Host fields n_rows / n_rem are updated at enqueue time.
- * Errors: INVALID_ARG, UNSUPPORTED (ratio != 4, dtype), CAPACITY.
+ * The old remainder followed by x is cut into groups of r consecutive rows;
+ * each whole group becomes one pooled row (mean of the r rows: float32 sum
+ * taken left to right, times the float32 value of 1/r, rounded to the
+ * storage type, ties to even), appended in place at cache->n_rows; the rows
+ * left over become the new remainder.  Host fields n_rows / n_rem are
+ * updated at enqueue time.
+ * Errors: INVALID_ARG, UNSUPPORTED (ratio outside [2, DSV4_MAX_RATIO],
+ * dtype), CAPACITY.
  */
 int dsv4_compress(dsv4_pool_cache* cache, const void* x, int64_t n_new, void* stream);
 
@@ -135,7 +143,7 @@ int dsv4_compress(dsv4_pool_cache* cache, const void* x, int64_t n_new, void* st
  * pooled-ratio causal mask folded into the score epilogue [P2 commit 5]);
  * fold_mask = 0: every s < S is scored (second-pass masking is then the
  * caller's, with the same -inf sentinel).
- * Shape gate: bf16 cache, dim in {32, 64, 128}, 1 <= n_heads <= 64,
+ * Shape gate: bf16 ratio-4 cache, dim in {32, 64, 128}, 1 <= n_heads <= 64,
  * S <= out_stride <= 2^28 - 64 (UNSUPPORTED beyond).
  */
 int dsv4_indexer_scores(const dsv4_pool_cache* index_cache, const void* q, const float* w,
@@ -181,16 +189,22 @@ int dsv4_indexer_select(const dsv4_pool_cache* index_cache, int64_t n_attn_rows,
 
 /*
  * Fused windowed + pooled prefill attention [P2 commit 1; P3 Possible design
- * step 4].  For the query at position p = q_pos0+t and head h:
+ * step 4].  For the query at position p = q_pos0+t and head h, with
+ * r = attn_cache->ratio:
  *   keys  = raw rows at positions max(0, p-window+1) .. p
- *           + pooled rows s listed in sel_idx[t] with 0 <= s < (p+1)/4
- *             (all s < (p+1)/4 when sel_idx is NULL; -1 slots are empty)
+ *           + pooled rows s listed in sel_idx[t] with 0 <= s < (p+1)/r
+ *             (all s < (p+1)/r when sel_idx is NULL; -1 slots are empty)
  *   out[t][h] = sum_j softmax_j(scale * q[t][h] . key_j) * key_j
  * (keys double as values and are shared by all heads).
  * q       : device bf16 [T][n_heads][head_dim]
  * raw_kv  : device bf16 [n_raw][head_dim], row i is position raw_pos0+i; it
  *           must cover [max(0, q_pos0-window+1), q_pos0+T).
- * attn_cache : bf16 pooling cache with dim == head_dim.
+ * attn_cache : bf16 pooling cache with dim == head_dim, or NULL for the
+ *           window-only mode (LocalAttention: no pooled keys; sel_idx must
+ *           then be NULL).  The three modes of [P2 commit 1]:
+ *           LocalAttention = NULL cache; CompressedAttention = ratio-128
+ *           cache, NULL sel_idx; SparseCompressedAttention = ratio-4 cache
+ *           with the indexer's sel_idx (or NULL on the small-pool path).
  * sel_idx : device int32 [T][topk] or NULL.
  * out     : device bf16 [T][n_heads][head_dim].
  * scale <= 0 selects 1/sqrt(head_dim).

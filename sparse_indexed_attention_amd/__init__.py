@@ -111,14 +111,17 @@ def _need(t: torch.Tensor, dtype, name: str, dims: int):
 
 
 class PoolCache:
-    """A PoolingCache: device rows [capacity, dim] and remainder [3, dim]
-    (torch tensors) plus the host struct the C ABI reads and updates."""
+    """A PoolingCache: device rows [capacity, dim] and remainder
+    [ratio - 1, dim] (torch tensors) plus the host struct the C ABI reads and
+    updates.  ratio 4 serves the indexer and sparse attention, ratio 128 the
+    CompressedAttention mode."""
 
-    def __init__(self, capacity: int, dim: int, dtype=torch.bfloat16, device="cuda"):
+    def __init__(self, capacity: int, dim: int, dtype=torch.bfloat16, device="cuda",
+                 ratio: int = RATIO):
         self.rows = torch.zeros((capacity, dim), dtype=dtype, device=device)
-        self.rem = torch.zeros((RATIO - 1, dim), dtype=dtype, device=device)
+        self.rem = torch.zeros((max(ratio - 1, 1), dim), dtype=dtype, device=device)
         self.struct = dsv4_pool_cache(self.rows.data_ptr(), self.rem.data_ptr(), capacity, 0, 0,
-                                      RATIO, dim, DSV4_BF16 if dtype == torch.bfloat16 else DSV4_F32)
+                                      ratio, dim, DSV4_BF16 if dtype == torch.bfloat16 else DSV4_F32)
 
     @property
     def n_rows(self) -> int:
@@ -135,6 +138,10 @@ class PoolCache:
     @property
     def capacity(self) -> int:
         return int(self.struct.capacity)
+
+    @property
+    def ratio(self) -> int:
+        return int(self.struct.ratio)
 
     def set_state(self, n_rows: int, n_rem: int = 0):
         """Declare rows [0, n_rows) and remainder [0, n_rem) valid (after the
@@ -211,8 +218,10 @@ def dsv4_indexer_select(index_cache: PoolCache, n_attn_rows: int, q, w, T: int, 
 
 
 def dsv4_sparse_prefill_attn(q: torch.Tensor, q_pos0: int, raw_kv: torch.Tensor, raw_pos0: int,
-                             window: int, attn_cache: PoolCache, sel_idx, out: torch.Tensor,
+                             window: int, attn_cache, sel_idx, out: torch.Tensor,
                              scale: float = 0.0, stream=None) -> None:
+    """attn_cache: a PoolCache, or None for window-only attention (then
+    sel_idx must be None too)."""
     _need(q, torch.bfloat16, "q", 3)
     _need(raw_kv, torch.bfloat16, "raw_kv", 2)
     _need(out, torch.bfloat16, "out", 3)
@@ -222,5 +231,6 @@ def dsv4_sparse_prefill_attn(q: torch.Tensor, q_pos0: int, raw_kv: torch.Tensor,
         topk = sel_idx.shape[1]
     _check(lib().dsv4_sparse_prefill_attn(_ptr(q), q.shape[0], q_pos0, q.shape[1], q.shape[2],
                                           scale, _ptr(raw_kv), raw_pos0, raw_kv.shape[0], window,
-                                          attn_cache.ref(), _ptr(sel_idx), topk, _ptr(out),
+                                          None if attn_cache is None else attn_cache.ref(),
+                                          _ptr(sel_idx), topk, _ptr(out),
                                           _stream(stream)))

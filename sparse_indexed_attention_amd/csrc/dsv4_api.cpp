@@ -37,9 +37,17 @@ int hip_status(hipError_t e, const char* what) {
   return fail(DSV4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-int check_cache(const dsv4_pool_cache* c, const char* name) {
+// Pool ratios accepted by the compressor and the attention: 4 (indexer and
+// sparse attention) and 128 (CompressedAttention) are the pages'; any ratio
+// in [2, DSV4_MAX_RATIO] follows the same definitions.  The indexer entry
+// points pass need_ratio = 4: their score mask and selection fill are the
+// ratio-4 rule.
+int check_cache(const dsv4_pool_cache* c, const char* name, int need_ratio = 0) {
   if (!c) return fail(DSV4_ERR_INVALID_ARG, "%s: NULL cache", name);
-  if (c->ratio != 4) return fail(DSV4_ERR_UNSUPPORTED, "%s: ratio %d (only 4)", name, c->ratio);
+  if (need_ratio && c->ratio != need_ratio)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: ratio %d (only %d)", name, c->ratio, need_ratio);
+  if (c->ratio < 2 || c->ratio > DSV4_MAX_RATIO)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: ratio %d", name, c->ratio);
   if (c->dtype != DSV4_BF16 && c->dtype != DSV4_F32)
     return fail(DSV4_ERR_UNSUPPORTED, "%s: dtype %d", name, c->dtype);
   if (c->dim <= 0) return fail(DSV4_ERR_INVALID_ARG, "%s: dim %d", name, c->dim);
@@ -53,7 +61,7 @@ int check_cache(const dsv4_pool_cache* c, const char* name) {
   return DSV4_OK;
 }
 
-inline int64_t vis_rows(int64_t p) { return (p + 1) / 4; }
+inline int64_t vis_rows(int64_t p, int ratio = 4) { return (p + 1) / ratio; }
 
 // The MFMA kernels read operands with 16-byte vector loads.
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -89,24 +97,24 @@ int dsv4_compress(dsv4_pool_cache* cache, const void* x, int64_t n_new, void* st
   if (n_new < 0) return fail(DSV4_ERR_INVALID_ARG, "compress: n_new %lld", (long long)n_new);
   if (n_new > 0 && !x) return fail(DSV4_ERR_INVALID_ARG, "compress: NULL input");
   const int64_t L = cache->n_rem + n_new;
-  const int64_t groups = L / 4;
+  const int64_t groups = L / cache->ratio;
   if (cache->n_rows + groups > cache->capacity)
     return fail(DSV4_ERR_CAPACITY, "compress: %lld + %lld rows exceed capacity %lld",
                 (long long)cache->n_rows, (long long)groups, (long long)cache->capacity);
   if (n_new == 0) return DSV4_OK;
   rc = hip_status(dsv4_launch_compress(cache->rows, cache->rem, cache->n_rows, cache->n_rem,
-                                       cache->dim, cache->dtype, x, n_new,
+                                       cache->ratio, cache->dim, cache->dtype, x, n_new,
                                        static_cast<hipStream_t>(stream)),
                   "compress launch");
   if (rc) return rc;
   cache->n_rows += groups;
-  cache->n_rem = static_cast<int32_t>(L - 4 * groups);
+  cache->n_rem = static_cast<int32_t>(L - cache->ratio * groups);
   return DSV4_OK;
 }
 
 static int check_scores_args(const dsv4_pool_cache* ic, const void* q, const float* w,
                              int64_t rows, int64_t q_pos0, int32_t n_heads, const char* who) {
-  int rc = check_cache(ic, who);
+  int rc = check_cache(ic, who, 4);
   if (rc) return rc;
   if (ic->dtype != DSV4_BF16) return fail(DSV4_ERR_UNSUPPORTED, "%s: index cache must be bf16", who);
   if (ic->dim != 32 && ic->dim != 64 && ic->dim != 128)
@@ -167,7 +175,7 @@ int dsv4_indexer_select(const dsv4_pool_cache* index_cache, int64_t n_attn_rows,
                         const float* w, int64_t T, int64_t q_pos0, int32_t n_heads, int32_t topk,
                         int32_t tile_rows, float* scratch, size_t scratch_bytes,
                         int32_t* out_idx, int32_t* out_all_pooled, void* stream) {
-  int rc = check_cache(index_cache, "indexer_select");
+  int rc = check_cache(index_cache, "indexer_select", 4);
   if (rc) return rc;
   const int64_t S = index_cache->n_rows;
   if (S != n_attn_rows)
@@ -226,15 +234,21 @@ int dsv4_sparse_prefill_attn(const void* q, int64_t T, int64_t q_pos0, int32_t n
                              int32_t head_dim, float scale, const void* raw_kv, int64_t raw_pos0,
                              int64_t n_raw, int32_t window, const dsv4_pool_cache* attn_cache,
                              const int32_t* sel_idx, int32_t topk, void* out, void* stream) {
-  int rc = check_cache(attn_cache, "sparse_prefill_attn");
-  if (rc) return rc;
-  if (attn_cache->dtype != DSV4_BF16)
-    return fail(DSV4_ERR_UNSUPPORTED, "sparse_prefill_attn: attention cache must be bf16");
   if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
     return fail(DSV4_ERR_UNSUPPORTED, "sparse_prefill_attn: head_dim %d", head_dim);
-  if (attn_cache->dim != head_dim)
-    return fail(DSV4_ERR_INVALID_ARG, "sparse_prefill_attn: cache dim %d != head_dim %d",
-                attn_cache->dim, head_dim);
+  // attn_cache == NULL is the window-only (LocalAttention) mode: no pooled
+  // keys, so no selection either.
+  if (attn_cache) {
+    int rc = check_cache(attn_cache, "sparse_prefill_attn");
+    if (rc) return rc;
+    if (attn_cache->dtype != DSV4_BF16)
+      return fail(DSV4_ERR_UNSUPPORTED, "sparse_prefill_attn: attention cache must be bf16");
+    if (attn_cache->dim != head_dim)
+      return fail(DSV4_ERR_INVALID_ARG, "sparse_prefill_attn: cache dim %d != head_dim %d",
+                  attn_cache->dim, head_dim);
+  } else if (sel_idx) {
+    return fail(DSV4_ERR_INVALID_ARG, "sparse_prefill_attn: selection given without a pool");
+  }
   if (n_heads < 1 || n_heads > DSV4_MAX_HEADS)
     return fail(DSV4_ERR_UNSUPPORTED, "sparse_prefill_attn: %d heads", n_heads);
   if (window < 1) return fail(DSV4_ERR_INVALID_ARG, "sparse_prefill_attn: window %d", window);
@@ -244,7 +258,7 @@ int dsv4_sparse_prefill_attn(const void* q, int64_t T, int64_t q_pos0, int32_t n
     return fail(DSV4_ERR_UNSUPPORTED, "sparse_prefill_attn: topk %d", topk);
   if (T == 0) return DSV4_OK;
   if (!q || !raw_kv || !out) return fail(DSV4_ERR_INVALID_ARG, "sparse_prefill_attn: NULL buffer");
-  if (!aligned16(q) || !aligned16(raw_kv) || !aligned16(attn_cache->rows))
+  if (!aligned16(q) || !aligned16(raw_kv) || (attn_cache && !aligned16(attn_cache->rows)))
     return fail(DSV4_ERR_INVALID_ARG,
                 "sparse_prefill_attn: q, raw_kv and cache rows must be 16-byte aligned");
   const int64_t need_lo = (q_pos0 - window + 1) > 0 ? (q_pos0 - window + 1) : 0;
@@ -254,13 +268,15 @@ int dsv4_sparse_prefill_attn(const void* q, int64_t T, int64_t q_pos0, int32_t n
                 "[%lld, %lld)",
                 (long long)raw_pos0, (long long)(raw_pos0 + n_raw), (long long)need_lo,
                 (long long)(q_pos0 + T));
-  if (vis_rows(q_pos0 + T - 1) > attn_cache->n_rows)
+  const int ratio = attn_cache ? attn_cache->ratio : 0;
+  if (attn_cache && vis_rows(q_pos0 + T - 1, ratio) > attn_cache->n_rows)
     return fail(DSV4_ERR_INVALID_ARG,
                 "sparse_prefill_attn: queries see %lld pooled rows, cache holds %lld",
-                (long long)vis_rows(q_pos0 + T - 1), (long long)attn_cache->n_rows);
+                (long long)vis_rows(q_pos0 + T - 1, ratio), (long long)attn_cache->n_rows);
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(head_dim));
   return hip_status(dsv4_launch_sparse_attn(q, T, q_pos0, n_heads, head_dim, sc, raw_kv, raw_pos0,
-                                            window, attn_cache->rows, sel_idx,
+                                            window, attn_cache ? attn_cache->rows : nullptr,
+                                            ratio, sel_idx,
                                             sel_idx ? topk : 0, out,
                                             static_cast<hipStream_t>(stream)),
                     "sparse_prefill_attn launch");

@@ -64,6 +64,11 @@ constexpr int64_t kMaxScoreStride = (int64_t(1) << 28) - 64;
 
 // Pooled rows visible to a query at absolute position p (ratio 4).
 __device__ __forceinline__ int64_t visible_rows(int64_t p) { return (p + 1) >> 2; }
+// The same rule for a pool of any ratio r >= 1: floor((p+1)/r); r == 0 means
+// no pool (the window-only mode), so nothing is visible.
+__device__ __forceinline__ int64_t visible_rows(int64_t p, int ratio) {
+  return ratio > 0 ? (p + 1) / ratio : 0;
+}
 
 // 16 bytes per lane from global memory straight into LDS
 // (global_load_lds_dwordx4): lane L of the wave writes lds_wave_base + 16*L.
@@ -102,8 +107,8 @@ __device__ __forceinline__ constexpr int wait_vmcnt(int n) { return 0x0F70 | (n 
 // Launch wrappers (defined next to their kernels).  All return hipError_t of
 // the launch; argument checks happen before they are called.
 hipError_t dsv4_launch_compress(void* rows, void* rem, int64_t n_rows, int32_t n_rem,
-                                int32_t dim, int32_t dtype, const void* x, int64_t n_new,
-                                hipStream_t s);
+                                int32_t ratio, int32_t dim, int32_t dtype, const void* x,
+                                int64_t n_new, hipStream_t s);
 hipError_t dsv4_launch_fill_sequential(int32_t* out, int64_t T, int64_t q_pos0, int64_t S,
                                        int32_t topk, hipStream_t s);
 hipError_t dsv4_launch_indexer_scores(const void* q, const float* w, const void* keys,
@@ -115,5 +120,5 @@ hipError_t dsv4_launch_topk(const float* scores, int64_t rows, int64_t stride, i
 hipError_t dsv4_launch_sparse_attn(const void* q, int64_t T, int64_t q_pos0, int32_t n_heads,
                                    int32_t head_dim, float scale, const void* raw_kv,
                                    int64_t raw_pos0, int32_t window, const void* pooled,
-                                   const int32_t* sel_idx, int32_t topk, void* out,
-                                   hipStream_t s);
+                                   int32_t ratio, const int32_t* sel_idx, int32_t topk,
+                                   void* out, hipStream_t s);

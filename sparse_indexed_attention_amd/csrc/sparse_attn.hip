@@ -8,9 +8,13 @@
 // mixed attention.]
 //
 // Per query p and head h, keys = raw rows p-window+1 .. p (clipped at 0) plus
-// the pooled rows listed in the query's selection with 0 <= s < (p+1)/4
+// the pooled rows listed in the query's selection with 0 <= s < (p+1)/r
 // (all of them when no selection is given); values are the keys (one KV row
-// shared by all heads); out = softmax(scale * q.K) . K.
+// shared by all heads); out = softmax(scale * q.K) . K.  The pool's ratio r
+// is 4 on the indexer path and 128 in the CompressedAttention mode; r = 0
+// (no pool) is the window-only LocalAttention mode [P2 commit 1: the same
+// kernel serves LocalAttention, CompressedAttention and
+// SparseCompressedAttention].
 //
 // Mapping onto CDNA4:
 //   * one workgroup per query; a wave owns 16 heads and one half of the head
@@ -78,8 +82,8 @@ template <int D, int NHG, int DSPLIT>
 __global__ void __launch_bounds__(NHG * DSPLIT * 64)
 sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float scale_log2,
                    const uint16_t* __restrict__ raw, int64_t raw_pos0, int window,
-                   const uint16_t* __restrict__ pooled, const int32_t* __restrict__ sel,
-                   int topk, uint16_t* __restrict__ out) {
+                   const uint16_t* __restrict__ pooled, int ratio,
+                   const int32_t* __restrict__ sel, int topk, uint16_t* __restrict__ out) {
   constexpr int NW = NHG * DSPLIT;
   constexpr int NT = NW * 64;
   constexpr int DH = D / DSPLIT;          // dims per wave
@@ -120,7 +124,7 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
   const int64_t p = q_pos0 + t;
   const int64_t lo = (p - window + 1) > 0 ? (p - window + 1) : 0;
   const int n_win = static_cast<int>(p - lo + 1);
-  const int64_t vis = visible_rows(p);
+  const int64_t vis = visible_rows(p, ratio);
   const uint16_t* self_row = raw + (p - raw_pos0) * D;  // always valid
 
   // ---- selection row into LDS; number of pooled slots to walk
@@ -155,21 +159,34 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
     return nullptr;
   };
 
-  // Gather tile `tile` into stage `buf`: instruction i moves rows
-  // i*RPI .. i*RPI+RPI-1, lane -> (row, slot).  Returns the tile's validity
-  // mask (bit k: key slot k has a row).  With one row per instruction, lane k
-  // looks up key k's row once and each instruction takes its row address from
-  // the owning lane (a wave-uniform base plus per-lane chunk offsets).
-  auto issue_tile = [&](int tile, int buf) -> uint32_t {
+  // Gather of a tile, in two parts so the row lookups can run an iteration
+  // ahead of the DMA issue.  lookup(tile): lane k (< 32) finds key slot k's
+  // row (the selection row in LDS, then the address); the ballot of found
+  // rows is the tile's validity mask (bit k: key slot k has a row).
+  struct Look {
+    uint32_t lo, hi;  // lane k's row address (RPI == 1)
+    uint32_t valid;
+    int tile;
+  };
+  auto lookup = [&](int tile) -> Look {
     const uint16_t* rk = lane < kKeys ? key_row(tile * kKeys + lane) : nullptr;
-    const uint32_t valid = static_cast<uint32_t>(__ballot(rk != nullptr));
+    Look lk;
+    lk.valid = static_cast<uint32_t>(__ballot(rk != nullptr));
+    const uint64_t ra = reinterpret_cast<uint64_t>(rk ? rk : self_row);
+    lk.lo = static_cast<uint32_t>(ra);
+    lk.hi = static_cast<uint32_t>(ra >> 32);
+    lk.tile = tile;
+    return lk;
+  };
+  // issue(lk, buf): instruction i moves rows i*RPI .. i*RPI+RPI-1 into stage
+  // `buf`.  With one row per instruction its address is wave-uniform: read
+  // from the owning lane, sent in the saddr form with per-lane chunk offsets.
+  auto issue = [&](const Look& lk, int buf) {
     if constexpr (RPI == 1) {
-      const uint64_t ra = reinterpret_cast<uint64_t>(rk ? rk : self_row);
-      const uint32_t ra_lo = static_cast<uint32_t>(ra), ra_hi = static_cast<uint32_t>(ra >> 32);
       for (int i = wave; i < INSTS; i += NW) {
         const uint64_t base =
-            (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ra_hi), i))) << 32) |
-            static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ra_lo), i));
+            (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lk.hi), i))) << 32) |
+            static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lk.lo), i));
         const uint32_t off = static_cast<uint32_t>(((lane % CPR) ^ swz(i)) * 16);
         global_to_lds16_s(reinterpret_cast<const void*>(base), off, &tiles[buf][i * D]);
       }
@@ -177,12 +194,11 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
       for (int i = wave; i < INSTS; i += NW) {
         const int row = i * RPI + lane / CPR;
         const int slot = lane % CPR;
-        const uint16_t* rp = key_row(tile * kKeys + row);
+        const uint16_t* rp = key_row(lk.tile * kKeys + row);
         if (!rp) rp = self_row;
         global_to_lds16(rp + (slot ^ swz(row)) * 8, &tiles[buf][i * RPI * D]);
       }
     }
-    return valid;
   };
 
   // ---- Q block (B operand of S^T = K.Q^T): lane group kb holds dims
@@ -305,8 +321,16 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
   // softmax VALU work.  Stage use at iteration `tile`: tile (P.V), tile+1
   // (QK), tile+2 (gather in flight, into the stage tile-1 released).
   // Validity masks of the tiles in flight: current, next, and the one after.
-  uint32_t vm_cur = issue_tile(0, 0);
-  uint32_t vm_next = n_tiles > 1 ? issue_tile(1, 1) : 0u;
+  Look lk = lookup(0);
+  issue(lk, 0);
+  uint32_t vm_cur = lk.valid;
+  uint32_t vm_next = 0u;
+  if (n_tiles > 1) {
+    lk = lookup(1);
+    issue(lk, 1);
+    vm_next = lk.valid;
+  }
+  if (n_tiles > 2) lk = lookup(2);  // the next tile to issue, looked up ahead
   f32x4_t s_own0, s_own1;  // this wave's partial S^T of the current tile
   if (n_tiles > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | kNewer);  // tile 0 landed; tile 1 may fly
   else __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -318,7 +342,12 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
     // publishes the partials of `tile` and the rows of tile+1; every wave
     // is done with tile-1, whose stage takes tile+2
     __syncthreads();
-    const uint32_t vm_after = tile + 2 < n_tiles ? issue_tile(tile + 2, (tile + 2) % kStages) : 0u;
+    uint32_t vm_after = 0u;
+    if (tile + 2 < n_tiles) {
+      issue(lk, (tile + 2) % kStages);
+      vm_after = lk.valid;
+      if (tile + 3 < n_tiles) lk = lookup(tile + 3);  // its latency hides under this tile's work
+    }
     const uint32_t vmask = vm_cur;
     vm_cur = vm_next;
     vm_next = vm_after;
@@ -406,17 +435,18 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
 template <int D, int NHG>
 hipError_t launch_hg(const dim3& grid, size_t dyn, hipStream_t s, const uint16_t* q, int64_t q_pos0,
                      int H, float sl2, const uint16_t* raw, int64_t raw_pos0, int window,
-                     const uint16_t* pooled, const int32_t* sel, int topk, uint16_t* out) {
+                     const uint16_t* pooled, int ratio, const int32_t* sel, int topk,
+                     uint16_t* out) {
   constexpr int DSPLIT = D >= 64 ? 2 : 1;
   hipLaunchKernelGGL((sparse_attn_kernel<D, NHG, DSPLIT>), grid, dim3(NHG * DSPLIT * 64), dyn, s,
-                     q, q_pos0, H, sl2, raw, raw_pos0, window, pooled, sel, topk, out);
+                     q, q_pos0, H, sl2, raw, raw_pos0, window, pooled, ratio, sel, topk, out);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const void* q, int64_t T, int64_t q_pos0, int H, float sl2, const void* raw,
-                    int64_t raw_pos0, int window, const void* pooled, const int32_t* sel,
-                    int topk, void* out, hipStream_t s) {
+                    int64_t raw_pos0, int window, const void* pooled, int ratio,
+                    const int32_t* sel, int topk, void* out, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(T));
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* rr = static_cast<const uint16_t*>(raw);
@@ -424,10 +454,10 @@ hipError_t launch_d(const void* q, int64_t T, int64_t q_pos0, int H, float sl2, 
   auto* oo = static_cast<uint16_t*>(out);
   const size_t dyn = static_cast<size_t>(sel ? topk : 0) * sizeof(int);
   switch ((H + 15) / 16) {
-    case 1: return launch_hg<D, 1>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, sel, topk, oo);
-    case 2: return launch_hg<D, 2>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, sel, topk, oo);
-    case 3: return launch_hg<D, 3>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, sel, topk, oo);
-    default: return launch_hg<D, 4>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, sel, topk, oo);
+    case 1: return launch_hg<D, 1>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, ratio, sel, topk, oo);
+    case 2: return launch_hg<D, 2>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, ratio, sel, topk, oo);
+    case 3: return launch_hg<D, 3>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, ratio, sel, topk, oo);
+    default: return launch_hg<D, 4>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, ratio, sel, topk, oo);
   }
 }
 
@@ -436,16 +466,16 @@ hipError_t launch_d(const void* q, int64_t T, int64_t q_pos0, int H, float sl2, 
 hipError_t dsv4_launch_sparse_attn(const void* q, int64_t T, int64_t q_pos0, int32_t n_heads,
                                    int32_t head_dim, float scale, const void* raw_kv,
                                    int64_t raw_pos0, int32_t window, const void* pooled,
-                                   const int32_t* sel_idx, int32_t topk, void* out,
-                                   hipStream_t s) {
+                                   int32_t ratio, const int32_t* sel_idx, int32_t topk,
+                                   void* out, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const float sl2 = scale * 1.4426950408889634f;
   switch (head_dim) {
-    case 32: return launch_d<32>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, sel_idx, topk, out, s);
-    case 64: return launch_d<64>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, sel_idx, topk, out, s);
-    case 128: return launch_d<128>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, sel_idx, topk, out, s);
-    case 256: return launch_d<256>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, sel_idx, topk, out, s);
-    case 512: return launch_d<512>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, sel_idx, topk, out, s);
+    case 32: return launch_d<32>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, ratio, sel_idx, topk, out, s);
+    case 64: return launch_d<64>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, ratio, sel_idx, topk, out, s);
+    case 128: return launch_d<128>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, ratio, sel_idx, topk, out, s);
+    case 256: return launch_d<256>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, ratio, sel_idx, topk, out, s);
+    case 512: return launch_d<512>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, ratio, sel_idx, topk, out, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -125,6 +125,17 @@ def make_inputs(wl: Workload, seed: int = 0, with_attn_q: bool = True) -> dict:
     return out
 
 
+def prefix_rows_ratio(wl: Workload, seed: int, ratio: int):
+    """Pooled prefix rows of a ratio-``ratio`` cache for ``wl`` (the
+    CompressedAttention pool at ratio 128): [prefix_tokens // ratio,
+    head_dim] drawn as N(0, 1/ratio), the law of a mean of ``ratio``
+    independent N(0, 1) rows, rounded to bf16.  Returns (torch CPU tensor,
+    float32 numpy values)."""
+    n = wl.prefix_tokens // ratio
+    a = normal(seed, f"prefix_attn_rows_r{ratio}", (n, wl.head_dim), float(1.0 / np.sqrt(ratio)))
+    return as_bf16(a)
+
+
 def as_bf16_values(a: np.ndarray) -> np.ndarray:
     """Values of ``a`` rounded to bf16 (used to feed a float32 tiny case to
     bf16-only kernels)."""

@@ -23,7 +23,7 @@ def test_library_exports_every_header_function():
 
 
 def test_abi_version_and_host_helpers():
-    assert dsv4.dsv4_abi_version() == 1
+    assert dsv4.dsv4_abi_version() == 2
     assert dsv4.dsv4_indexer_all_pooled(0, 8) is False
     assert dsv4.dsv4_indexer_all_pooled(1, 8) is True
     assert dsv4.dsv4_indexer_all_pooled(8, 8) is True
@@ -51,8 +51,16 @@ def test_compress_validation_leaves_state():
     assert "capacity" in dsv4.dsv4_last_error()
     assert _rc("dsv4_compress", ctypes.byref(c), None, 1, None) == INVALID
     assert _rc("dsv4_compress", ctypes.byref(c), ctypes.c_void_p(FAKE), -1, None) == INVALID
-    bad = _cache(ratio=128)
-    assert _rc("dsv4_compress", ctypes.byref(bad), ctypes.c_void_p(FAKE), 4, None) == UNSUPPORTED
+    for r in (0, 1, 257):
+        bad = _cache(ratio=r)
+        assert _rc("dsv4_compress", ctypes.byref(bad), ctypes.c_void_p(FAKE), 4, None) == UNSUPPORTED
+    # ratio 128: 100 waiting + 200 new = 2 rows -> 17 > 16; the remainder
+    # bound follows the ratio (127 may wait, 128 may not)
+    big = _cache(n_rows=15, n_rem=100, ratio=128)
+    assert _rc("dsv4_compress", ctypes.byref(big), ctypes.c_void_p(FAKE), 200, None) == CAPACITY
+    assert (big.n_rows, big.n_rem) == (15, 100)
+    assert _rc("dsv4_compress", ctypes.byref(_cache(n_rem=128, ratio=128)),
+               ctypes.c_void_p(FAKE), 4, None) == INVALID
     bad = _cache(n_rem=4)
     assert _rc("dsv4_compress", ctypes.byref(bad), ctypes.c_void_p(FAKE), 4, None) == INVALID
     assert _rc("dsv4_compress", None, ctypes.c_void_p(FAKE), 4, None) == INVALID
@@ -94,6 +102,9 @@ def test_scores_and_topk_gates():
     c = _cache(n_rows=10, dim=128)
     assert _rc("dsv4_indexer_scores", ctypes.byref(c), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
                4, 0, 64, 1, ctypes.c_void_p(FAKE), 8, None) == INVALID  # stride < rows
+    c = _cache(n_rows=10, dim=128, ratio=128)  # the indexer's mask is the ratio-4 rule
+    assert _rc("dsv4_indexer_scores", ctypes.byref(c), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+               4, 0, 64, 1, ctypes.c_void_p(FAKE), 64, None) == UNSUPPORTED
     # top-k: visible prefix of the last row (position 99 -> 25 rows) exceeds 20 columns
     assert _rc("dsv4_topk_select", ctypes.c_void_p(FAKE), 4, 64, 96, 20, 8,
                ctypes.c_void_p(FAKE), None) == INVALID
@@ -119,3 +130,16 @@ def test_attention_gates():
     assert call(topk=0) == UNSUPPORTED
     f32 = _cache(n_rows=40, dim=512, cap=64, dtype=2)
     assert call(cache=f32) == UNSUPPORTED
+    # ratio-128 pool: position 5119 sees 40 rows (fits), 5120+ sees 40 too,
+    # 5247 sees 41 > 40
+    r128 = _cache(n_rows=40, dim=512, cap=64, ratio=128)
+    assert call(cache=r128, q_pos0=5244, raw_pos0=5117, n_raw=131) == INVALID
+    assert "41 pooled rows" in dsv4.dsv4_last_error()
+    # window-only mode: no pool, so no selection either
+    assert _rc("dsv4_sparse_prefill_attn", ctypes.c_void_p(FAKE), 4, 100, 64, 512, 0.0,
+               ctypes.c_void_p(FAKE), 0, 104, 128, None, ctypes.c_void_p(FAKE), 16,
+               ctypes.c_void_p(FAKE), None) == INVALID
+    assert "without a pool" in dsv4.dsv4_last_error()
+    assert _rc("dsv4_sparse_prefill_attn", ctypes.c_void_p(FAKE), 4, 100, 64, 96, 0.0,
+               ctypes.c_void_p(FAKE), 0, 104, 128, None, None, 0,
+               ctypes.c_void_p(FAKE), None) == UNSUPPORTED
