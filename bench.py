@@ -146,6 +146,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the CPU oracle baseline (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--matrix", action="store_true",
+                    help="instead of the benchmark, time the (global chunk, indexer tile) matrix "
+                         "at 1M context, serial and ping-pong, one JSON line per pair")
     ap.add_argument("--no-modes", action="store_true",
                     help="skip the local / ratio-128 attention mode measurements")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -265,6 +268,78 @@ def measure_modes(setup: Setup, reps: int) -> dict:
     return res
 
 
+# (global chunk, indexer tile) pairs of the tiling proposal's benchmark matrix
+MATRIX = ((4096, 4096), (2048, 2048), (1024, 1024), (4096, 2048), (4096, 1024))
+
+
+def tile_matrix(steps: int):
+    """Each (chunk, tile) pair at 1M tokens of context (the chunk ends at
+    position 2^20): score scratch bytes, whole-chunk indexer select time with
+    one scratch reused by every tile (serial), the same tiles with two scratch
+    buffers and the top-k of tile i on a second stream beside the scoring of
+    tile i+1 (ping-pong), and the whole step (compress, select, attention)."""
+    import dataclasses
+    for chunk, tile in MATRIX:
+        wl = dataclasses.replace(SI.CTX_1M, name=f"ctx1m-chunk{chunk}-tile{tile}",
+                                 prefix_tokens=(1 << 20) - chunk, chunk=chunk,
+                                 tile_rows=0 if tile == chunk else tile)
+        st = Setup(wl, 0)
+        d = st.dsv4
+        st.step()
+        torch.cuda.synchronize()
+        S, T, q0 = st.S_after, wl.chunk, wl.q_pos0
+        stride = d.dsv4_score_stride(S)
+        bufs = [st.scratch[:st.tile * stride].view(st.tile, stride)]
+        n_tiles = (T + st.tile - 1) // st.tile
+        if n_tiles > 1:
+            bufs.append(torch.empty(st.tile * stride, device="cuda").view(st.tile, stride))
+        main, aux = torch.cuda.current_stream(), torch.cuda.Stream()
+
+        def serial():
+            d.dsv4_indexer_select(st.icache, st.acache.n_rows, st.q_idx, st.w, T, q0,
+                                  wl.idx_heads, wl.topk, st.idx, st.scratch, wl.tile_rows)
+
+        def pingpong():
+            ev_sc = [torch.cuda.Event() for _ in bufs]
+            ev_tk = [torch.cuda.Event() for _ in bufs]
+            start = torch.cuda.Event()
+            start.record(main)
+            aux.wait_event(start)
+            for i, t0 in enumerate(range(0, T, st.tile)):
+                b, n = i % len(bufs), min(st.tile, T - t0)
+                if i >= len(bufs):
+                    main.wait_event(ev_tk[b])
+                d.dsv4_indexer_scores(st.icache, st.q_idx[t0:t0 + n], st.w[t0:t0 + n], q0 + t0,
+                                      bufs[b][:n], True, stream=main)
+                ev_sc[b].record(main)
+                aux.wait_event(ev_sc[b])
+                d.dsv4_topk_select(bufs[b][:n], q0 + t0, S, wl.topk, st.idx[t0:t0 + n],
+                                   stream=aux)
+                ev_tk[b].record(aux)
+            for e in ev_tk:
+                main.wait_event(e)
+
+        serial()
+        torch.cuda.synchronize()
+        ref = st.idx.clone()
+        pingpong()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(ref, st.idx))
+        ms_serial = timed_kernel(serial, steps)
+        ms_pp = timed_kernel(pingpong, steps)
+        ms_step = timed_kernel(st.step, steps)
+        one = d.dsv4_indexer_scratch_bytes(st.tile, S)
+        print(json.dumps({
+            "workload": wl.name, "context_tokens": q0 + T, "chunk": T, "tile_rows": st.tile,
+            "pooled_rows": S, "scratch_bytes": one, "pingpong_scratch_bytes": one * len(bufs),
+            "select_ms": ms_serial, "select_rows_per_s": T / (ms_serial * 1e-3),
+            "pingpong_select_ms": ms_pp, "pingpong_equal_selection": same,
+            "step_ms": ms_step, "step_rows_per_s": T / (ms_step * 1e-3)}))
+        sys.stdout.flush()
+        del st, bufs
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(setup: Setup, budget_s: float):
     """The CPU oracle (score + top-k) on a bounded sample of the chunk's query rows."""
     from oracle import dsv4_oracle as O
@@ -334,8 +409,11 @@ def main():
         print("bench.py measures one GPU only: the hot path runs on one MI355X and this build "
               "has no multi-GPU path (see the sharding note in the design notes).", file=sys.stderr)
         sys.exit(2)
-    wl = SI.WORKLOADS[args.workload]
     torch.cuda.init()
+    if args.matrix:
+        tile_matrix(max(3, args.steps // 4))
+        return
+    wl = SI.WORKLOADS[args.workload]
     setup = Setup(wl, args.seed)
     d = setup.dsv4
     T = wl.chunk
