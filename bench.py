@@ -150,7 +150,7 @@ def parse():
                     help="instead of the benchmark, time the (global chunk, indexer tile) matrix "
                          "at 1M context, serial and ping-pong, one JSON line per pair")
     ap.add_argument("--no-modes", action="store_true",
-                    help="skip the local / ratio-128 attention mode measurements")
+                    help="skip the sibling-mode and narrow-query measurements")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after the benchmark, run a 1 GiB copy kernel three times (counter scale)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "OUT_MD"),
@@ -265,6 +265,42 @@ def measure_modes(setup: Setup, reps: int) -> dict:
                                   "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS},
                      "gather_GBps": gbs}
     res["compress_r128_ms"] = ms_c128
+    return res
+
+
+def measure_narrow(setup: Setup, reps: int) -> dict:
+    """Narrow-query steps (T = 1, 2, 4 query rows: decode, draft verification,
+    short prefill bands) at the end of this workload's context, against the
+    same caches: the indexer select (scratch as dsv4_indexer_scratch_bytes
+    sizes it) and the key-split attention with its planned split count.
+    HIP-event means over `reps` calls of each."""
+    d, wl = setup.dsv4, setup.wl
+    S = setup.S_after
+    H, D, W, k = wl.heads, wl.head_dim, wl.window, wl.topk
+    res = {}
+    for T in (1, 2, 4):
+        q0 = 4 * S - T                      # the last T positions the caches cover
+        scratch = torch.empty(d.dsv4_indexer_scratch_bytes(T, S) // 4, device="cuda")
+        idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        out = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+        qi, w, qa = setup.q_idx[:T], setup.w[:T], setup.q_attn[:T]
+        ns, nb = d.dsv4_sparse_attn_narrow_plan(T, H, D, W, k)
+        ws = torch.empty(max(nb // 4, 4), device="cuda")
+        raw_lo = q0 - W + 1
+        raw = setup.raw_kv[raw_lo - setup.raw_pos0:q0 + T - setup.raw_pos0]
+
+        def sel():
+            d.dsv4_indexer_select(setup.icache, setup.acache.n_rows, qi, w, T, q0, wl.idx_heads,
+                                  k, idx, scratch, 0)
+
+        def attn():
+            d.dsv4_sparse_attn_narrow(qa, q0, raw, raw_lo, W, setup.acache, idx, out, ns, ws)
+
+        ms_sel = timed_kernel(sel, reps)
+        ms_attn = timed_kernel(attn, reps)
+        ms_step = timed_kernel(lambda: (sel(), attn()), reps)
+        res[f"T{T}"] = {"select_ms": ms_sel, "attention_ms": ms_attn, "attention_splits": ns,
+                        "step_ms": ms_step, "query_rows_per_s": T / (ms_step * 1e-3)}
     return res
 
 
@@ -459,6 +495,7 @@ def main():
     attn_tflops = attn_flops / (attn * 1e-3) / 1e12
 
     modes = measure_modes(setup, max(5, args.steps // 2)) if not args.no_modes else None
+    narrow = measure_narrow(setup, max(10, args.steps)) if not args.no_modes else None
     cpu = cpu_baseline(setup, args.cpu_seconds) if args.cpu_seconds > 0 else None
     rec = {
         "metric": "indexer score+top-k query rows/s and pooled-row scores/s at 128K ctx; MFMA util",
@@ -491,6 +528,7 @@ def main():
         "attn_roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                           "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS},
         "modes": modes,
+        "narrow": narrow,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec))

@@ -11,6 +11,8 @@
  *        [Summary commits 1, 4, 5; Performance]
  *   [P3] "[Discussion] Tile indexed-attention scoring independently of the
  *        global prefill chunk" (ds4 issue 644) [Summary, Possible design]
+ *   [P4] "perf(dflash): add opt-in exact prefill bands" (lucebox pull
+ *        request 590) [q2-q4 exact prefill bands]
  *
  * Conventions shared by every entry point
  *   - Pointers named "device" are HIP device memory owned by the caller; the
@@ -26,8 +28,9 @@
  *     visibility rebuilt from positions [P2 commit 1]); they never take a mask
  *     tensor.  A caller needing another mask must use its own path.
  *   - Positions are absolute token positions counted from the start of the
- *     stream (0-based).  Pooled row s summarises tokens 4s .. 4s+3 and is
- *     visible to a query at position p iff 4(s+1) <= p+1, i.e. s < (p+1)/4.
+ *     stream (0-based).  With pool ratio r (4 unless stated), pooled row s
+ *     summarises tokens rs .. rs+r-1 and is visible to a query at position p
+ *     iff r(s+1) <= p+1, i.e. s < (p+1)/r.
  *   - Calls that touch the same cache must be ordered on one stream.
  */
 #ifndef DSV4_H
@@ -40,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DSV4_ABI_VERSION 2
+#define DSV4_ABI_VERSION 3
 
 /* Return codes. */
 #define DSV4_OK                0
@@ -63,6 +66,7 @@ extern "C" {
 #define DSV4_MAX_INDEX_HEADS 64
 #define DSV4_MAX_HEADS       64
 #define DSV4_MAX_RATIO       256
+#define DSV4_MAX_ATTN_SPLITS 64
 
 /*
  * PoolingCache of one compressor [P1 Summary, Correctness; P2 commit 4].
@@ -111,7 +115,10 @@ int64_t dsv4_score_stride(int64_t n_rows);
 /*
  * Bytes of score scratch dsv4_indexer_select needs for query-row tiles of
  * tile_rows rows against up to max_rows pooled rows [P3 Summary: scratch
- * scales with tile rows x pooled rows].  Writes *bytes.  0 or INVALID_ARG.
+ * scales with tile rows x pooled rows]: tile_rows x dsv4_score_stride(max_rows)
+ * floats, plus, for narrow tiles (tile_rows <= 64) over more than 32,768
+ * pooled rows, the workspace of the chunk-parallel top-k (sized for
+ * DSV4_MAX_TOPK).  Writes *bytes.  0 or INVALID_ARG.
  */
 int dsv4_indexer_scratch_bytes(int64_t tile_rows, int64_t max_rows, size_t* bytes);
 
@@ -164,6 +171,26 @@ int dsv4_topk_select(const float* scores, int64_t rows, int64_t stride, int64_t 
                      int64_t n_cols, int32_t topk, int32_t* out_idx, void* stream);
 
 /*
+ * Chunk-parallel top-k for a few long rows (narrow-query steps: decode,
+ * draft verification, short prefill bands at long context [P1 scope; P4]).
+ * Same arguments, rule and output as dsv4_topk_select, bit for bit, plus a
+ * caller-owned device workspace (16-byte aligned).  When 1 <= rows <= 64,
+ * the longest visible prefix spans more than one 32,768-column chunk and
+ * the first row sees at least topk columns, every (row, chunk) pair is
+ * selected by its own workgroup and a second pass selects each row's top-k
+ * among the chunk winners; otherwise it runs dsv4_topk_select's kernel and
+ * the workspace is unused (may be NULL).
+ * dsv4_topk_split_workspace_bytes writes the workspace bytes needed (0 when
+ * the two-pass path does not apply).
+ * Errors: as dsv4_topk_select; INVALID_ARG (workspace NULL / misaligned when
+ * needed), SCRATCH (workspace too small).
+ */
+int dsv4_topk_split_workspace_bytes(int64_t rows, int64_t q_pos0, int32_t topk, size_t* bytes);
+int dsv4_topk_select_split(const float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
+                           int64_t n_cols, int32_t topk, int32_t* out_idx, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
  * Whole indexer step for one prefill chunk of T query rows [P1 Summary;
  * P3 Possible design].
  *   1. Guard: index_cache->n_rows must equal n_attn_rows (ROW_MISMATCH).
@@ -172,7 +199,11 @@ int dsv4_topk_select(const float* scores, int64_t rows, int64_t stride, int64_t 
  *   3. If S == 0: every slot -1, *out_all_pooled = 0.
  *   4. Otherwise, for each tile of tile_rows query rows (0 = all T), scores
  *      are written to `scratch` (folded mask) and the tile's top-k is taken,
- *      reusing the same scratch for every tile; *out_all_pooled = 0.
+ *      reusing the same scratch for every tile; *out_all_pooled = 0.  A
+ *      narrow tile (<= 64 rows) over more than 32,768 pooled rows uses the
+ *      chunk-parallel top-k of dsv4_topk_select_split when the scratch also
+ *      holds its workspace (as dsv4_indexer_scratch_bytes sizes it), with
+ *      the same result.
  * q, w        : as dsv4_indexer_scores, T rows.
  * scratch     : device float, >= dsv4_indexer_scratch_bytes(tile, S) bytes
  *               (may be NULL on paths 2 and 3).
@@ -216,6 +247,47 @@ int dsv4_sparse_prefill_attn(const void* q, int64_t T, int64_t q_pos0, int32_t n
                              const void* raw_kv, int64_t raw_pos0, int64_t n_raw,
                              int32_t window, const dsv4_pool_cache* attn_cache,
                              const int32_t* sel_idx, int32_t topk, void* out, void* stream);
+
+/*
+ * Narrow-query steps (T = 1-4 and other short query counts: decode, draft
+ * verification, narrow prefill bands) [P1 scope: MTP with three draft
+ * tokens; P4: exact q2-q4 prefill bands].  dsv4_sparse_prefill_attn walks each query's keys in one
+ * workgroup, so a handful of queries occupies a handful of CUs; the narrow
+ * variant splits each query's key tiles over n_splits workgroups and merges
+ * them.  The result is the same attention (same keys, same definition), up
+ * to floating-point summation order.
+ *
+ * Plan: *n_splits = the split count to use for T queries of at most
+ * window + n_pooled_keys keys each (n_pooled_keys: topk with a selection, the
+ * visible pooled rows without one, 0 for window only), about one workgroup
+ * per CU in all and at least two 32-key tiles per split, at most
+ * DSV4_MAX_ATTN_SPLITS; *workspace_bytes = the workspace it needs (0 when
+ * *n_splits == 1).  0 or INVALID_ARG.
+ */
+int dsv4_sparse_attn_narrow_plan(int64_t T, int32_t n_heads, int32_t head_dim, int32_t window,
+                                 int64_t n_pooled_keys, int32_t* n_splits,
+                                 size_t* workspace_bytes);
+
+/*
+ * Narrow-query attention: arguments, modes and output as
+ * dsv4_sparse_prefill_attn, plus
+ * n_splits  : 1 .. DSV4_MAX_ATTN_SPLITS key splits per query (1 = the
+ *             prefill kernel itself; the workspace is then unused).
+ * workspace : device, 16-byte aligned, >= T*n_splits*n_heads*(head_dim+2)*4
+ *             bytes, owned by the caller (fp32 partial outputs, then the
+ *             per-head (max, sum) pairs); its contents are overwritten.
+ * Each split walks a balanced range of the query's key tiles with the same
+ * online softmax and leaves (m, l, O); a second kernel merges the splits:
+ * out = sum_s 2^(m_s-M) O_s / sum_s 2^(m_s-M) l_s, M = max m_s.
+ * Errors: as dsv4_sparse_prefill_attn; UNSUPPORTED (n_splits), INVALID_ARG
+ * (workspace NULL / misaligned), SCRATCH (workspace too small).
+ */
+int dsv4_sparse_attn_narrow(const void* q, int64_t T, int64_t q_pos0, int32_t n_heads,
+                            int32_t head_dim, float scale,
+                            const void* raw_kv, int64_t raw_pos0, int64_t n_raw,
+                            int32_t window, const dsv4_pool_cache* attn_cache,
+                            const int32_t* sel_idx, int32_t topk, int32_t n_splits,
+                            float* workspace, size_t workspace_bytes, void* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,8 @@ __all__ = [
     "DSV4Error", "PoolCache", "lib", "header_functions",
     "dsv4_abi_version", "dsv4_last_error", "dsv4_indexer_all_pooled", "dsv4_score_stride",
     "dsv4_indexer_scratch_bytes", "dsv4_compress", "dsv4_indexer_scores", "dsv4_topk_select",
-    "dsv4_indexer_select", "dsv4_sparse_prefill_attn",
+    "dsv4_indexer_select", "dsv4_sparse_prefill_attn", "dsv4_sparse_attn_narrow_plan",
+    "dsv4_sparse_attn_narrow", "dsv4_topk_split_workspace_bytes", "dsv4_topk_select_split",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +60,14 @@ _SIGNATURES = {
     "dsv4_sparse_prefill_attn": (c_i32, [c_vp, c_i64, c_i64, c_i32, c_i32, c_f32, c_vp, c_i64,
                                          c_i64, c_i32, ctypes.POINTER(dsv4_pool_cache), c_vp,
                                          c_i32, c_vp, c_vp]),
+    "dsv4_topk_split_workspace_bytes": (c_i32, [c_i64, c_i64, c_i32, ctypes.POINTER(c_sz)]),
+    "dsv4_topk_select_split": (c_i32, [c_vp, c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_sz,
+                                       c_vp]),
+    "dsv4_sparse_attn_narrow_plan": (c_i32, [c_i64, c_i32, c_i32, c_i32, c_i64,
+                                             ctypes.POINTER(c_i32), ctypes.POINTER(c_sz)]),
+    "dsv4_sparse_attn_narrow": (c_i32, [c_vp, c_i64, c_i64, c_i32, c_i32, c_f32, c_vp, c_i64,
+                                        c_i64, c_i32, ctypes.POINTER(dsv4_pool_cache), c_vp,
+                                        c_i32, c_i32, c_vp, c_sz, c_vp, c_vp]),
 }
 
 _lib = None
@@ -200,6 +209,25 @@ def dsv4_topk_select(scores: torch.Tensor, q_pos0: int, n_cols: int, topk: int,
                                   topk, _ptr(out_idx), _stream(stream)))
 
 
+def dsv4_topk_split_workspace_bytes(rows: int, q_pos0: int, topk: int) -> int:
+    nb = c_sz(0)
+    _check(lib().dsv4_topk_split_workspace_bytes(rows, q_pos0, topk, ctypes.byref(nb)))
+    return int(nb.value)
+
+
+def dsv4_topk_select_split(scores: torch.Tensor, q_pos0: int, n_cols: int, topk: int,
+                           out_idx: torch.Tensor, workspace=None, stream=None) -> None:
+    """Chunk-parallel top-k (same result as dsv4_topk_select); workspace: a
+    CUDA tensor of at least dsv4_topk_split_workspace_bytes bytes, or None
+    when that is 0."""
+    _need(scores, torch.float32, "scores", 2)
+    _need(out_idx, torch.int32, "out_idx", 2)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dsv4_topk_select_split(_ptr(scores), scores.shape[0], scores.shape[1], q_pos0,
+                                        n_cols, topk, _ptr(out_idx), _ptr(workspace), nbytes,
+                                        _stream(stream)))
+
+
 def dsv4_indexer_select(index_cache: PoolCache, n_attn_rows: int, q, w, T: int, q_pos0: int,
                         n_heads: int, topk: int, out_idx: torch.Tensor, scratch=None,
                         tile_rows: int = 0, stream=None) -> bool:
@@ -234,3 +262,36 @@ def dsv4_sparse_prefill_attn(q: torch.Tensor, q_pos0: int, raw_kv: torch.Tensor,
                                           None if attn_cache is None else attn_cache.ref(),
                                           _ptr(sel_idx), topk, _ptr(out),
                                           _stream(stream)))
+
+
+def dsv4_sparse_attn_narrow_plan(T: int, n_heads: int, head_dim: int, window: int,
+                                 n_pooled_keys: int):
+    """(n_splits, workspace_bytes) for narrow-query attention."""
+    ns, nb = c_i32(0), c_sz(0)
+    _check(lib().dsv4_sparse_attn_narrow_plan(T, n_heads, head_dim, window, n_pooled_keys,
+                                              ctypes.byref(ns), ctypes.byref(nb)))
+    return int(ns.value), int(nb.value)
+
+
+def dsv4_sparse_attn_narrow(q: torch.Tensor, q_pos0: int, raw_kv: torch.Tensor, raw_pos0: int,
+                            window: int, attn_cache, sel_idx, out: torch.Tensor, n_splits: int,
+                            workspace=None, scale: float = 0.0, stream=None) -> None:
+    """Narrow-query attention: as dsv4_sparse_prefill_attn, with each query's
+    keys split over n_splits workgroups (workspace: a float32 CUDA tensor of
+    at least the planned bytes, or None when n_splits == 1)."""
+    _need(q, torch.bfloat16, "q", 3)
+    _need(raw_kv, torch.bfloat16, "raw_kv", 2)
+    _need(out, torch.bfloat16, "out", 3)
+    topk = 0
+    if sel_idx is not None:
+        _need(sel_idx, torch.int32, "sel_idx", 2)
+        topk = sel_idx.shape[1]
+    nbytes = 0
+    if workspace is not None:
+        _need(workspace, torch.float32, "workspace", 1)
+        nbytes = workspace.numel() * 4
+    _check(lib().dsv4_sparse_attn_narrow(_ptr(q), q.shape[0], q_pos0, q.shape[1], q.shape[2],
+                                         scale, _ptr(raw_kv), raw_pos0, raw_kv.shape[0], window,
+                                         None if attn_cache is None else attn_cache.ref(),
+                                         _ptr(sel_idx), topk, n_splits, _ptr(workspace), nbytes,
+                                         _ptr(out), _stream(stream)))

@@ -20,6 +20,8 @@
 #include "../../include/dsv4.h"
 #include "dsv4_device.h"
 
+static_assert(DSV4_MAX_ATTN_SPLITS == dsv4::kMaxAttnSplits, "split cap");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -63,6 +65,23 @@ int check_cache(const dsv4_pool_cache* c, const char* name, int need_ratio = 0) 
 
 inline int64_t vis_rows(int64_t p, int ratio = 4) { return (p + 1) / ratio; }
 
+// Chunk-parallel top-k (two passes) serves at most kSplitRows rows whose
+// visible prefixes span more than one 32,768-column chunk and hold at least
+// topk columns; its workspace is the chunk candidates' columns and scores.
+constexpr int64_t kSplitRows = 64;
+constexpr int64_t kTopkChunk = 32768;
+
+size_t split_ws_bytes(int64_t rows, int64_t chunks, int32_t topk) {
+  const size_t one = (static_cast<size_t>(rows) * static_cast<size_t>(chunks) *
+                          static_cast<size_t>(topk) * 4 + 15) & ~static_cast<size_t>(15);
+  return 2 * one;
+}
+
+bool split_applies(int64_t rows, int64_t q_pos0, int32_t topk) {
+  return rows > 0 && rows <= kSplitRows && dsv4_topk_split_chunks(rows, q_pos0) >= 2 &&
+         (q_pos0 + 1) / 4 >= topk;
+}
+
 // The MFMA kernels read operands with 16-byte vector loads.
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -88,6 +107,9 @@ int dsv4_indexer_scratch_bytes(int64_t tile_rows, int64_t max_rows, size_t* byte
     return fail(DSV4_ERR_INVALID_ARG, "scratch_bytes: bad arguments");
   *bytes = static_cast<size_t>(tile_rows) * static_cast<size_t>(dsv4_score_stride(max_rows)) *
            sizeof(float);
+  // narrow tiles over long rows: room for the chunk-parallel top-k as well
+  if (tile_rows > 0 && tile_rows <= kSplitRows && max_rows > kTopkChunk)
+    *bytes += split_ws_bytes(tile_rows, (max_rows + kTopkChunk - 1) / kTopkChunk, DSV4_MAX_TOPK);
   return DSV4_OK;
 }
 
@@ -154,21 +176,70 @@ int dsv4_indexer_scores(const dsv4_pool_cache* index_cache, const void* q, const
                     "indexer_scores launch");
 }
 
+static int check_topk_args(const char* who, const float* scores, int64_t rows, int64_t stride,
+                           int64_t q_pos0, int64_t n_cols, int32_t topk,
+                           const int32_t* out_idx) {
+  if (rows < 0 || q_pos0 < 0 || n_cols < 0 || stride < n_cols)
+    return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", who);
+  if (topk < 1 || topk > DSV4_MAX_TOPK)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: topk %d", who, topk);
+  if (rows == 0) return DSV4_OK;
+  if (!out_idx) return fail(DSV4_ERR_INVALID_ARG, "%s: NULL out", who);
+  if (vis_rows(q_pos0 + rows - 1) > n_cols)
+    return fail(DSV4_ERR_INVALID_ARG, "%s: visible prefix %lld exceeds %lld columns", who,
+                (long long)vis_rows(q_pos0 + rows - 1), (long long)n_cols);
+  if (n_cols > 0 && !scores) return fail(DSV4_ERR_INVALID_ARG, "%s: NULL scores", who);
+  return DSV4_OK;
+}
+
 int dsv4_topk_select(const float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
                      int64_t n_cols, int32_t topk, int32_t* out_idx, void* stream) {
-  if (rows < 0 || q_pos0 < 0 || n_cols < 0 || stride < n_cols)
-    return fail(DSV4_ERR_INVALID_ARG, "topk_select: bad sizes");
-  if (topk < 1 || topk > DSV4_MAX_TOPK)
-    return fail(DSV4_ERR_UNSUPPORTED, "topk_select: topk %d", topk);
-  if (rows == 0) return DSV4_OK;
-  if (!out_idx) return fail(DSV4_ERR_INVALID_ARG, "topk_select: NULL out");
-  if (vis_rows(q_pos0 + rows - 1) > n_cols)
-    return fail(DSV4_ERR_INVALID_ARG, "topk_select: visible prefix %lld exceeds %lld columns",
-                (long long)vis_rows(q_pos0 + rows - 1), (long long)n_cols);
-  if (n_cols > 0 && !scores) return fail(DSV4_ERR_INVALID_ARG, "topk_select: NULL scores");
+  int rc = check_topk_args("topk_select", scores, rows, stride, q_pos0, n_cols, topk, out_idx);
+  if (rc || rows == 0) return rc;
   return hip_status(dsv4_launch_topk(scores, rows, stride, q_pos0, topk, out_idx,
                                      static_cast<hipStream_t>(stream)),
                     "topk launch");
+}
+
+int dsv4_topk_split_workspace_bytes(int64_t rows, int64_t q_pos0, int32_t topk, size_t* bytes) {
+  if (!bytes || rows < 0 || q_pos0 < 0 || topk < 1 || topk > DSV4_MAX_TOPK)
+    return fail(DSV4_ERR_INVALID_ARG, "topk_split_workspace_bytes: bad arguments");
+  *bytes = split_applies(rows, q_pos0, topk)
+               ? split_ws_bytes(rows, dsv4_topk_split_chunks(rows, q_pos0), topk)
+               : 0;
+  return DSV4_OK;
+}
+
+// Chunk-parallel top-k when it applies (workspace checked), else the
+// one-workgroup-per-row kernel.
+static int launch_topk_any(const char* who, const float* scores, int64_t rows, int64_t stride,
+                           int64_t q_pos0, int32_t topk, int32_t* out_idx, void* workspace,
+                           size_t workspace_bytes, hipStream_t s) {
+  if (!split_applies(rows, q_pos0, topk))
+    return hip_status(dsv4_launch_topk(scores, rows, stride, q_pos0, topk, out_idx, s),
+                      "topk launch");
+  const int64_t chunks = dsv4_topk_split_chunks(rows, q_pos0);
+  const size_t need = split_ws_bytes(rows, chunks, topk);
+  if (!workspace || !aligned16(workspace))
+    return fail(DSV4_ERR_INVALID_ARG, "%s: workspace NULL or not 16-byte aligned", who);
+  if (workspace_bytes < need)
+    return fail(DSV4_ERR_SCRATCH, "%s: workspace %zu bytes, need %zu", who, workspace_bytes,
+                need);
+  auto* cidx = static_cast<int32_t*>(workspace);
+  auto* csc = reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2);
+  return hip_status(dsv4_launch_topk_split(scores, rows, stride, q_pos0, topk, out_idx, cidx,
+                                           csc, s),
+                    "topk split launch");
+}
+
+int dsv4_topk_select_split(const float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
+                           int64_t n_cols, int32_t topk, int32_t* out_idx, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  int rc = check_topk_args("topk_select_split", scores, rows, stride, q_pos0, n_cols, topk,
+                           out_idx);
+  if (rc || rows == 0) return rc;
+  return launch_topk_any("topk_select_split", scores, rows, stride, q_pos0, topk, out_idx,
+                         workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 int dsv4_indexer_select(const dsv4_pool_cache* index_cache, int64_t n_attn_rows, const void* q,
@@ -221,12 +292,74 @@ int dsv4_indexer_select(const dsv4_pool_cache* index_cache, int64_t n_attn_rows,
                                                scratch, stride, s),
                     "indexer_scores launch");
     if (rc) return rc;
-    rc = hip_status(dsv4_launch_topk(scratch, rows, stride, q_pos0 + t0, topk,
-                                     out_idx + t0 * topk, s),
-                    "topk launch");
+    // a narrow tile over long rows takes the chunk-parallel top-k when the
+    // scratch holds its workspace after the tile's scores
+    const bool split = split_applies(rows, q_pos0 + t0, topk) &&
+                       scratch_bytes >= need + split_ws_bytes(rows,
+                                                              dsv4_topk_split_chunks(rows, q_pos0 + t0),
+                                                              topk);
+    if (split)
+      rc = launch_topk_any("indexer_select", scratch, rows, stride, q_pos0 + t0, topk,
+                           out_idx + t0 * topk, reinterpret_cast<char*>(scratch) + need,
+                           scratch_bytes - need, s);
+    else
+      rc = hip_status(dsv4_launch_topk(scratch, rows, stride, q_pos0 + t0, topk,
+                                       out_idx + t0 * topk, s),
+                      "topk launch");
     if (rc) return rc;
   }
   if (out_all_pooled) *out_all_pooled = 0;
+  return DSV4_OK;
+}
+
+// Argument checks shared by the attention entry points (all before any
+// enqueue).  *empty is set when there is nothing to do (T == 0).
+static int check_attn_args(const char* who, const void* q, int64_t T, int64_t q_pos0,
+                           int32_t n_heads, int32_t head_dim, const void* raw_kv,
+                           int64_t raw_pos0, int64_t n_raw, int32_t window,
+                           const dsv4_pool_cache* attn_cache, const int32_t* sel_idx,
+                           int32_t topk, const void* out, bool* empty) {
+  *empty = false;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: head_dim %d", who, head_dim);
+  // attn_cache == NULL is the window-only (LocalAttention) mode: no pooled
+  // keys, so no selection either.
+  if (attn_cache) {
+    int rc = check_cache(attn_cache, who);
+    if (rc) return rc;
+    if (attn_cache->dtype != DSV4_BF16)
+      return fail(DSV4_ERR_UNSUPPORTED, "%s: attention cache must be bf16", who);
+    if (attn_cache->dim != head_dim)
+      return fail(DSV4_ERR_INVALID_ARG, "%s: cache dim %d != head_dim %d", who, attn_cache->dim,
+                  head_dim);
+  } else if (sel_idx) {
+    return fail(DSV4_ERR_INVALID_ARG, "%s: selection given without a pool", who);
+  }
+  if (n_heads < 1 || n_heads > DSV4_MAX_HEADS)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: %d heads", who, n_heads);
+  if (window < 1) return fail(DSV4_ERR_INVALID_ARG, "%s: window %d", who, window);
+  if (T < 0 || q_pos0 < 0 || raw_pos0 < 0 || n_raw < 0)
+    return fail(DSV4_ERR_INVALID_ARG, "%s: negative size", who);
+  if (sel_idx && (topk < 1 || topk > DSV4_MAX_TOPK))
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: topk %d", who, topk);
+  if (T == 0) {
+    *empty = true;
+    return DSV4_OK;
+  }
+  if (!q || !raw_kv || !out) return fail(DSV4_ERR_INVALID_ARG, "%s: NULL buffer", who);
+  if (!aligned16(q) || !aligned16(raw_kv) || (attn_cache && !aligned16(attn_cache->rows)))
+    return fail(DSV4_ERR_INVALID_ARG, "%s: q, raw_kv and cache rows must be 16-byte aligned",
+                who);
+  const int64_t need_lo = (q_pos0 - window + 1) > 0 ? (q_pos0 - window + 1) : 0;
+  if (raw_pos0 > need_lo || raw_pos0 + n_raw < q_pos0 + T)
+    return fail(DSV4_ERR_INVALID_ARG,
+                "%s: raw rows [%lld, %lld) do not cover window positions [%lld, %lld)", who,
+                (long long)raw_pos0, (long long)(raw_pos0 + n_raw), (long long)need_lo,
+                (long long)(q_pos0 + T));
+  if (attn_cache && vis_rows(q_pos0 + T - 1, attn_cache->ratio) > attn_cache->n_rows)
+    return fail(DSV4_ERR_INVALID_ARG, "%s: queries see %lld pooled rows, cache holds %lld", who,
+                (long long)vis_rows(q_pos0 + T - 1, attn_cache->ratio),
+                (long long)attn_cache->n_rows);
   return DSV4_OK;
 }
 
@@ -234,52 +367,78 @@ int dsv4_sparse_prefill_attn(const void* q, int64_t T, int64_t q_pos0, int32_t n
                              int32_t head_dim, float scale, const void* raw_kv, int64_t raw_pos0,
                              int64_t n_raw, int32_t window, const dsv4_pool_cache* attn_cache,
                              const int32_t* sel_idx, int32_t topk, void* out, void* stream) {
-  if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
-    return fail(DSV4_ERR_UNSUPPORTED, "sparse_prefill_attn: head_dim %d", head_dim);
-  // attn_cache == NULL is the window-only (LocalAttention) mode: no pooled
-  // keys, so no selection either.
-  if (attn_cache) {
-    int rc = check_cache(attn_cache, "sparse_prefill_attn");
-    if (rc) return rc;
-    if (attn_cache->dtype != DSV4_BF16)
-      return fail(DSV4_ERR_UNSUPPORTED, "sparse_prefill_attn: attention cache must be bf16");
-    if (attn_cache->dim != head_dim)
-      return fail(DSV4_ERR_INVALID_ARG, "sparse_prefill_attn: cache dim %d != head_dim %d",
-                  attn_cache->dim, head_dim);
-  } else if (sel_idx) {
-    return fail(DSV4_ERR_INVALID_ARG, "sparse_prefill_attn: selection given without a pool");
-  }
-  if (n_heads < 1 || n_heads > DSV4_MAX_HEADS)
-    return fail(DSV4_ERR_UNSUPPORTED, "sparse_prefill_attn: %d heads", n_heads);
-  if (window < 1) return fail(DSV4_ERR_INVALID_ARG, "sparse_prefill_attn: window %d", window);
-  if (T < 0 || q_pos0 < 0 || raw_pos0 < 0 || n_raw < 0)
-    return fail(DSV4_ERR_INVALID_ARG, "sparse_prefill_attn: negative size");
-  if (sel_idx && (topk < 1 || topk > DSV4_MAX_TOPK))
-    return fail(DSV4_ERR_UNSUPPORTED, "sparse_prefill_attn: topk %d", topk);
-  if (T == 0) return DSV4_OK;
-  if (!q || !raw_kv || !out) return fail(DSV4_ERR_INVALID_ARG, "sparse_prefill_attn: NULL buffer");
-  if (!aligned16(q) || !aligned16(raw_kv) || (attn_cache && !aligned16(attn_cache->rows)))
-    return fail(DSV4_ERR_INVALID_ARG,
-                "sparse_prefill_attn: q, raw_kv and cache rows must be 16-byte aligned");
-  const int64_t need_lo = (q_pos0 - window + 1) > 0 ? (q_pos0 - window + 1) : 0;
-  if (raw_pos0 > need_lo || raw_pos0 + n_raw < q_pos0 + T)
-    return fail(DSV4_ERR_INVALID_ARG,
-                "sparse_prefill_attn: raw rows [%lld, %lld) do not cover window positions "
-                "[%lld, %lld)",
-                (long long)raw_pos0, (long long)(raw_pos0 + n_raw), (long long)need_lo,
-                (long long)(q_pos0 + T));
-  const int ratio = attn_cache ? attn_cache->ratio : 0;
-  if (attn_cache && vis_rows(q_pos0 + T - 1, ratio) > attn_cache->n_rows)
-    return fail(DSV4_ERR_INVALID_ARG,
-                "sparse_prefill_attn: queries see %lld pooled rows, cache holds %lld",
-                (long long)vis_rows(q_pos0 + T - 1, ratio), (long long)attn_cache->n_rows);
+  bool empty = false;
+  int rc = check_attn_args("sparse_prefill_attn", q, T, q_pos0, n_heads, head_dim, raw_kv,
+                           raw_pos0, n_raw, window, attn_cache, sel_idx, topk, out, &empty);
+  if (rc || empty) return rc;
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(head_dim));
   return hip_status(dsv4_launch_sparse_attn(q, T, q_pos0, n_heads, head_dim, sc, raw_kv, raw_pos0,
                                             window, attn_cache ? attn_cache->rows : nullptr,
-                                            ratio, sel_idx,
-                                            sel_idx ? topk : 0, out,
+                                            attn_cache ? attn_cache->ratio : 0, sel_idx,
+                                            sel_idx ? topk : 0, out, 1, nullptr, nullptr,
                                             static_cast<hipStream_t>(stream)),
                     "sparse_prefill_attn launch");
+}
+
+// Bytes of narrow-attention workspace for T queries split n_splits ways:
+// fp32 O [T][n_splits][n_heads][head_dim], then (m, l) [T][n_splits][n_heads][2].
+static size_t narrow_ws_bytes(int64_t T, int32_t n_splits, int32_t n_heads, int32_t head_dim) {
+  return static_cast<size_t>(T) * static_cast<size_t>(n_splits) * static_cast<size_t>(n_heads) *
+         (static_cast<size_t>(head_dim) + 2) * sizeof(float);
+}
+
+int dsv4_sparse_attn_narrow_plan(int64_t T, int32_t n_heads, int32_t head_dim, int32_t window,
+                                 int64_t n_pooled_keys, int32_t* n_splits,
+                                 size_t* workspace_bytes) {
+  if (!n_splits || !workspace_bytes || T < 0 || n_heads < 1 || head_dim < 1 || window < 1 ||
+      n_pooled_keys < 0)
+    return fail(DSV4_ERR_INVALID_ARG, "sparse_attn_narrow_plan: bad arguments");
+  // About one workgroup per CU in all (256), each with at least two 32-key
+  // tiles, at most DSV4_MAX_ATTN_SPLITS splits.
+  const int64_t tiles = (static_cast<int64_t>(window) + n_pooled_keys + 31) / 32;
+  int64_t ns = T > 0 ? (256 + T - 1) / T : 1;
+  if (ns > tiles / 2) ns = tiles / 2;
+  if (ns > DSV4_MAX_ATTN_SPLITS) ns = DSV4_MAX_ATTN_SPLITS;
+  if (ns < 1) ns = 1;
+  *n_splits = static_cast<int32_t>(ns);
+  *workspace_bytes = ns > 1 ? narrow_ws_bytes(T, *n_splits, n_heads, head_dim) : 0;
+  return DSV4_OK;
+}
+
+int dsv4_sparse_attn_narrow(const void* q, int64_t T, int64_t q_pos0, int32_t n_heads,
+                            int32_t head_dim, float scale, const void* raw_kv, int64_t raw_pos0,
+                            int64_t n_raw, int32_t window, const dsv4_pool_cache* attn_cache,
+                            const int32_t* sel_idx, int32_t topk, int32_t n_splits,
+                            float* workspace, size_t workspace_bytes, void* out, void* stream) {
+  bool empty = false;
+  int rc = check_attn_args("sparse_attn_narrow", q, T, q_pos0, n_heads, head_dim, raw_kv,
+                           raw_pos0, n_raw, window, attn_cache, sel_idx, topk, out, &empty);
+  if (rc) return rc;
+  if (n_splits < 1 || n_splits > DSV4_MAX_ATTN_SPLITS)
+    return fail(DSV4_ERR_UNSUPPORTED, "sparse_attn_narrow: %d splits", n_splits);
+  if (empty) return DSV4_OK;
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (n_splits > 1) {
+    const size_t need = narrow_ws_bytes(T, n_splits, n_heads, head_dim);
+    if (!workspace || !aligned16(workspace))
+      return fail(DSV4_ERR_INVALID_ARG, "sparse_attn_narrow: workspace NULL or not 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(DSV4_ERR_SCRATCH, "sparse_attn_narrow: workspace %zu bytes, need %zu",
+                  workspace_bytes, need);
+    part_o = workspace;
+    part_ml = workspace + static_cast<size_t>(T) * n_splits * n_heads * head_dim;
+  }
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(head_dim));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = hip_status(dsv4_launch_sparse_attn(q, T, q_pos0, n_heads, head_dim, sc, raw_kv, raw_pos0,
+                                          window, attn_cache ? attn_cache->rows : nullptr,
+                                          attn_cache ? attn_cache->ratio : 0, sel_idx,
+                                          sel_idx ? topk : 0, out, n_splits, part_o, part_ml, s),
+                  "sparse_attn_narrow launch");
+  if (rc || n_splits == 1) return rc;
+  return hip_status(dsv4_launch_attn_combine(part_o, part_ml, T, n_splits, n_heads, head_dim, out, s),
+                    "sparse_attn_narrow combine launch");
 }
 
 }  // extern "C"

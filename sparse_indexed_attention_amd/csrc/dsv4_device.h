@@ -60,6 +60,9 @@ __device__ __forceinline__ float relu_bits(float x) {
 
 // Largest score-row stride (floats) the score kernel accepts: two rows of it
 // must fit a 32-bit buffer range.
+// Most key splits of one query in the narrow-query attention (one wave
+// merges their states).
+constexpr int kMaxAttnSplits = 64;
 constexpr int64_t kMaxScoreStride = (int64_t(1) << 28) - 64;
 
 // Pooled rows visible to a query at absolute position p (ratio 4).
@@ -117,8 +120,19 @@ hipError_t dsv4_launch_indexer_scores(const void* q, const float* w, const void*
                                       int64_t out_stride, hipStream_t s);
 hipError_t dsv4_launch_topk(const float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
                             int32_t topk, int32_t* out_idx, hipStream_t s);
+// Chunk-parallel top-k of a few long rows (two passes; see topk.hip): the
+// number of 32,768-column chunks of the longest row, and the launch, which
+// needs cand_idx / cand_score of rows * chunks * topk entries each.
+int64_t dsv4_topk_split_chunks(int64_t rows, int64_t q_pos0);
+hipError_t dsv4_launch_topk_split(const float* scores, int64_t rows, int64_t stride,
+                                  int64_t q_pos0, int32_t topk, int32_t* out_idx,
+                                  int32_t* cand_idx, float* cand_score, hipStream_t s);
 hipError_t dsv4_launch_sparse_attn(const void* q, int64_t T, int64_t q_pos0, int32_t n_heads,
                                    int32_t head_dim, float scale, const void* raw_kv,
                                    int64_t raw_pos0, int32_t window, const void* pooled,
                                    int32_t ratio, const int32_t* sel_idx, int32_t topk,
-                                   void* out, hipStream_t s);
+                                   void* out, int32_t nsplit, float* part_o, float* part_ml,
+                                   hipStream_t s);
+hipError_t dsv4_launch_attn_combine(const float* part_o, const float* part_ml, int64_t T,
+                                    int32_t nsplit, int32_t n_heads, int32_t head_dim, void* out,
+                                    hipStream_t s);

@@ -341,9 +341,14 @@ hipError_t launch_t(const void* q, const float* w, const void* keys, int64_t row
   const int cgroups = nqb >= 16 ? 4 : 8;
   const int64_t qgroups = 8 / cgroups;
   const int64_t nqb_g = (nqb + qgroups - 1) / qgroups;  // query blocks per query group
-  // Column splits per column group: enough workgroups to fill 256 CUs several
-  // times, and at least one tile per split.
-  int64_t per_cg = (4096 + 8 * nqb_g - 1) / (8 * nqb_g);
+  // Column splits per column group.  About two workgroups per CU in total
+  // (512) for narrow query counts, four (1,024) from 32 query blocks up:
+  // every workgroup re-reads its queries and runs a pipeline prologue, so
+  // more, shorter splits lose (at 64 query rows, 4,096 one-tile splits take
+  // twice as long as 256 long ones), while fewer than one round over the
+  // CUs leaves the chip idle.  At least one tile per split.
+  const int64_t target_wg = nqb >= 32 ? 1024 : 512;
+  int64_t per_cg = (target_wg + 8 * nqb_g - 1) / (8 * nqb_g);
   int64_t max_per_cg = S / (static_cast<int64_t>(cgroups) * kTileCols);
   if (max_per_cg < 1) max_per_cg = 1;
   if (per_cg > max_per_cg) per_cg = max_per_cg;

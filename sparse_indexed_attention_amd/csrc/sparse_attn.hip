@@ -83,7 +83,8 @@ __global__ void __launch_bounds__(NHG * DSPLIT * 64)
 sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float scale_log2,
                    const uint16_t* __restrict__ raw, int64_t raw_pos0, int window,
                    const uint16_t* __restrict__ pooled, int ratio,
-                   const int32_t* __restrict__ sel, int topk, uint16_t* __restrict__ out) {
+                   const int32_t* __restrict__ sel, int topk, uint16_t* __restrict__ out,
+                   int nsplit, float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int NW = NHG * DSPLIT;
   constexpr int NT = NW * 64;
   constexpr int DH = D / DSPLIT;          // dims per wave
@@ -121,11 +122,25 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
   const int l16 = lane & 15;
 
   const int64_t t = blockIdx.x;
+  const int split = blockIdx.y;  // key split (nsplit > 1: partial results)
   const int64_t p = q_pos0 + t;
   const int64_t lo = (p - window + 1) > 0 ? (p - window + 1) : 0;
   const int n_win = static_cast<int>(p - lo + 1);
   const int64_t vis = visible_rows(p, ratio);
   const uint16_t* self_row = raw + (p - raw_pos0) * D;  // always valid
+
+  // ---- Q block (B operand of S^T = K.Q^T): lane group kb holds dims
+  // dh*DH + kb*DH/4 .. + DH/4 over the KSTEP steps.  Loaded first, so its
+  // latency overlaps the selection row's.
+  const int head = hg * 16 + l16;
+  const bool hv = head < H;
+  bf16x8_t qf[KSTEP];
+  {
+    const uint16_t* qp = q + ((t * H + head) * (int64_t)D + dh * DH + kb * (DH / 4));
+#pragma unroll
+    for (int j = 0; j < KSTEP; ++j)
+      qf[j] = hv ? *reinterpret_cast<const bf16x8_t*>(qp + j * 8) : bf16x8_t{};
+  }
 
   // ---- selection row into LDS; number of pooled slots to walk
   int n_slots;
@@ -147,7 +162,12 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
     n_slots = static_cast<int>(vis);
   }
   const int n_keys = n_win + n_slots;
-  const int n_tiles = (n_keys + kKeys - 1) / kKeys;
+  const int n_tiles_all = (n_keys + kKeys - 1) / kKeys;
+  // This workgroup's tiles: all of them, or split `split` of nsplit balanced
+  // ranges (a range may be empty when there are fewer tiles than splits).
+  const int tile_lo = static_cast<int>((static_cast<int64_t>(split) * n_tiles_all) / nsplit);
+  const int n_tiles =
+      static_cast<int>((static_cast<int64_t>(split + 1) * n_tiles_all) / nsplit) - tile_lo;
 
   auto key_row = [&](int j) -> const uint16_t* {  // row of key slot j, or nullptr
     if (j < n_win) return raw + (lo + j - raw_pos0) * D;
@@ -201,18 +221,7 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
     }
   };
 
-  // ---- Q block (B operand of S^T = K.Q^T): lane group kb holds dims
-  // dh*DH + kb*DH/4 .. + DH/4 over the KSTEP steps
-  const int head = hg * 16 + l16;
-  const bool hv = head < H;
-  bf16x8_t qf[KSTEP];
-  {
-    const uint16_t* qp = q + ((t * H + head) * (int64_t)D + dh * DH + kb * (DH / 4));
-#pragma unroll
-    for (int j = 0; j < KSTEP; ++j)
-      qf[j] = hv ? *reinterpret_cast<const bf16x8_t*>(qp + j * 8) : bf16x8_t{};
-  }
-  // Drain the compiler's own loads (Q) before the first LDS DMA is issued, so
+  // Drain the compiler's own loads (Q, selection) before the first LDS DMA is issued, so
   // the only vector-memory operations in flight inside the loop are the tile
   // gathers the loop accounts for.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -321,91 +330,115 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
   // softmax VALU work.  Stage use at iteration `tile`: tile (P.V), tile+1
   // (QK), tile+2 (gather in flight, into the stage tile-1 released).
   // Validity masks of the tiles in flight: current, next, and the one after.
-  Look lk = lookup(0);
-  issue(lk, 0);
-  uint32_t vm_cur = lk.valid;
-  uint32_t vm_next = 0u;
-  if (n_tiles > 1) {
-    lk = lookup(1);
-    issue(lk, 1);
-    vm_next = lk.valid;
-  }
-  if (n_tiles > 2) lk = lookup(2);  // the next tile to issue, looked up ahead
-  f32x4_t s_own0, s_own1;  // this wave's partial S^T of the current tile
-  if (n_tiles > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | kNewer);  // tile 0 landed; tile 1 may fly
-  else __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();  // publishes tile 0
-  qk(0, s_own0, s_own1);
-  put_partial(0, s_own0, s_own1);
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's gather of tile+1 (issued last) landed
-    // publishes the partials of `tile` and the rows of tile+1; every wave
-    // is done with tile-1, whose stage takes tile+2
-    __syncthreads();
-    uint32_t vm_after = 0u;
-    if (tile + 2 < n_tiles) {
-      issue(lk, (tile + 2) % kStages);
-      vm_after = lk.valid;
-      if (tile + 3 < n_tiles) lk = lookup(tile + 3);  // its latency hides under this tile's work
+  // An empty split (fewer tiles than splits) skips the pipeline and leaves
+  // the empty softmax state (o = 0, m = -inf, l = 0).
+  if (n_tiles > 0) {
+    // Tile indices below are local to the split (stages and parities); the
+    // lookups take the split's global tile index tile_lo + local.
+    Look lk = lookup(tile_lo);
+    issue(lk, 0);
+    uint32_t vm_cur = lk.valid;
+    uint32_t vm_next = 0u;
+    if (n_tiles > 1) {
+      lk = lookup(tile_lo + 1);
+      issue(lk, 1);
+      vm_next = lk.valid;
     }
-    const uint32_t vmask = vm_cur;
-    vm_cur = vm_next;
-    vm_next = vm_after;
+    if (n_tiles > 2) lk = lookup(tile_lo + 2);  // the next tile to issue, looked up ahead
+    f32x4_t s_own0, s_own1;  // this wave's partial S^T of the current tile
+    if (n_tiles > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | kNewer);  // tile 0 landed; tile 1 may fly
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();  // publishes tile 0
+    qk(0, s_own0, s_own1);
+    put_partial(0, s_own0, s_own1);
+    for (int tile = 0; tile < n_tiles; ++tile) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's gather of tile+1 (issued last) landed
+      // publishes the partials of `tile` and the rows of tile+1; every wave
+      // is done with tile-1, whose stage takes tile+2
+      __syncthreads();
+      uint32_t vm_after = 0u;
+      if (tile + 2 < n_tiles) {
+        issue(lk, (tile + 2) % kStages);
+        vm_after = lk.valid;
+        if (tile + 3 < n_tiles) lk = lookup(tile_lo + tile + 3);  // latency hides under this tile
+      }
+      const uint32_t vmask = vm_cur;
+      vm_cur = vm_next;
+      vm_next = vm_after;
 
-    f32x4_t sacc0 = s_own0, sacc1 = s_own1;
-    add_partner(tile, sacc0, sacc1);
-    // the next tile's partial S^T: its MFMAs overlap the softmax below
-    if (tile + 1 < n_tiles) qk(tile + 1, s_own0, s_own1);
+      f32x4_t sacc0 = s_own0, sacc1 = s_own1;
+      add_partner(tile, sacc0, sacc1);
+      // the next tile's partial S^T: its MFMAs overlap the softmax below
+      if (tile + 1 < n_tiles) qk(tile + 1, s_own0, s_own1);
 
-    // lane holds, for head l16, keys mt*16 + 4*i + kb (output rows 4*kb + i)
-    float sv[8];
-    float mx = -INFINITY;
+      // lane holds, for head l16, keys mt*16 + 4*i + kb (output rows 4*kb + i)
+      float sv[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k0 = 4 * i + kb, k1 = 16 + 4 * i + kb;
+        sv[i] = ((vmask >> k0) & 1u) ? sacc0[i] * scale_log2 : -INFINITY;
+        sv[4 + i] = ((vmask >> k1) & 1u) ? sacc1[i] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, fmaxf(sv[i], sv[4 + i]));
+      }
+      mx = xor16_32_max(mx);
+      // Lazy rescale: exponentials are taken against a reference max m_ref that
+      // only moves when the running max passes it by more than kSlack (log2
+      // units); p <= 2^kSlack stays far from fp32 / bf16 overflow.
+      const bool bump = mx > m_ref + kSlack;
+      const float m_new = bump ? mx : m_ref;
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      float psum = 0.f;
+      float pr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);  // v_exp_f32 (tiny results flush to 0)
+        psum += pr[i];
+      }
+      psum = xor16_32_sum(psum);
+      bf16x8_t pa;
+      {
+        uint32_t pk[4];
+        pk[0] = pack_bf16x2(pr[0], pr[1]);
+        pk[1] = pack_bf16x2(pr[2], pr[3]);
+        pk[2] = pack_bf16x2(pr[4], pr[5]);
+        pk[3] = pack_bf16x2(pr[6], pr[7]);
+        pa = *reinterpret_cast<const bf16x8_t*>(pk);
+      }
+      if (tile + 1 < n_tiles) put_partial(tile + 1, s_own0, s_own1);
+      if (__ballot(bump)) {
+        const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
+        l_run *= alpha;
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kb + i);
+#pragma unroll
+        for (int n = 0; n < NTILE; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[n][i] *= al[i];
+      }
+      m_ref = m_new;
+      l_run += psum;
+      pv(tile, pa);
+    }
+  }
+  if (nsplit > 1) {
+    // ---- partial state of this split: O unnormalised (fp32, relative to
+    // m_ref), and m_ref (log2 units) and l per head
+    float* po = part_o + ((t * nsplit + split) * H) * static_cast<int64_t>(D);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int k0 = 4 * i + kb, k1 = 16 + 4 * i + kb;
-      sv[i] = ((vmask >> k0) & 1u) ? sacc0[i] * scale_log2 : -INFINITY;
-      sv[4 + i] = ((vmask >> k1) & 1u) ? sacc1[i] * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, fmaxf(sv[i], sv[4 + i]));
-    }
-    mx = xor16_32_max(mx);
-    // Lazy rescale: exponentials are taken against a reference max m_ref that
-    // only moves when the running max passes it by more than kSlack (log2
-    // units); p <= 2^kSlack stays far from fp32 / bf16 overflow.
-    const bool bump = mx > m_ref + kSlack;
-    const float m_new = bump ? mx : m_ref;
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    float psum = 0.f;
-    float pr[8];
+      const int hh = hg * 16 + 4 * kb + i;
+      if (hh < H) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pr[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);  // v_exp_f32 (tiny results flush to 0)
-      psum += pr[i];
+        for (int n = 0; n < NTILE; ++n) po[hh * static_cast<int64_t>(D) + dh * DH + n * 16 + l16] = o[n][i];
+      }
     }
-    psum = xor16_32_sum(psum);
-    bf16x8_t pa;
-    {
-      uint32_t pk[4];
-      pk[0] = pack_bf16x2(pr[0], pr[1]);
-      pk[1] = pack_bf16x2(pr[2], pr[3]);
-      pk[2] = pack_bf16x2(pr[4], pr[5]);
-      pk[3] = pack_bf16x2(pr[6], pr[7]);
-      pa = *reinterpret_cast<const bf16x8_t*>(pk);
+    if (dh == 0 && kb == 0 && hv) {
+      part_ml[((t * nsplit + split) * H + head) * 2] = m_ref;
+      part_ml[((t * nsplit + split) * H + head) * 2 + 1] = l_run;
     }
-    if (tile + 1 < n_tiles) put_partial(tile + 1, s_own0, s_own1);
-    if (__ballot(bump)) {
-      const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
-      l_run *= alpha;
-      float al[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kb + i);
-#pragma unroll
-      for (int n = 0; n < NTILE; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[n][i] *= al[i];
-    }
-    m_ref = m_new;
-    l_run += psum;
-    pv(tile, pa);
+    return;
   }
   __syncthreads();  // every wave is done with the tile stages
 
@@ -436,46 +469,121 @@ template <int D, int NHG>
 hipError_t launch_hg(const dim3& grid, size_t dyn, hipStream_t s, const uint16_t* q, int64_t q_pos0,
                      int H, float sl2, const uint16_t* raw, int64_t raw_pos0, int window,
                      const uint16_t* pooled, int ratio, const int32_t* sel, int topk,
-                     uint16_t* out) {
+                     uint16_t* out, int nsplit, float* part_o, float* part_ml) {
   constexpr int DSPLIT = D >= 64 ? 2 : 1;
   hipLaunchKernelGGL((sparse_attn_kernel<D, NHG, DSPLIT>), grid, dim3(NHG * DSPLIT * 64), dyn, s,
-                     q, q_pos0, H, sl2, raw, raw_pos0, window, pooled, ratio, sel, topk, out);
+                     q, q_pos0, H, sl2, raw, raw_pos0, window, pooled, ratio, sel, topk, out,
+                     nsplit, part_o, part_ml);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const void* q, int64_t T, int64_t q_pos0, int H, float sl2, const void* raw,
                     int64_t raw_pos0, int window, const void* pooled, int ratio,
-                    const int32_t* sel, int topk, void* out, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(T));
+                    const int32_t* sel, int topk, void* out, int nsplit, float* part_o,
+                    float* part_ml, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>(nsplit));
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* rr = static_cast<const uint16_t*>(raw);
   const auto* pp = static_cast<const uint16_t*>(pooled);
   auto* oo = static_cast<uint16_t*>(out);
   const size_t dyn = static_cast<size_t>(sel ? topk : 0) * sizeof(int);
   switch ((H + 15) / 16) {
-    case 1: return launch_hg<D, 1>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, ratio, sel, topk, oo);
-    case 2: return launch_hg<D, 2>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, ratio, sel, topk, oo);
-    case 3: return launch_hg<D, 3>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, ratio, sel, topk, oo);
-    default: return launch_hg<D, 4>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, ratio, sel, topk, oo);
+    case 1: return launch_hg<D, 1>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, ratio, sel, topk, oo, nsplit, part_o, part_ml);
+    case 2: return launch_hg<D, 2>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, ratio, sel, topk, oo, nsplit, part_o, part_ml);
+    case 3: return launch_hg<D, 3>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, ratio, sel, topk, oo, nsplit, part_o, part_ml);
+    default: return launch_hg<D, 4>(grid, dyn, s, qq, q_pos0, H, sl2, rr, raw_pos0, window, pp, ratio, sel, topk, oo, nsplit, part_o, part_ml);
+  }
+}
+
+// Merge of the key splits of one query's attention.  Split s left, per head,
+// its reference max m_s (log2 units), its sum l_s of 2^(logit - m_s), and O_s
+// = sum of 2^(logit - m_s) * value (fp32, unnormalised; zero for an empty
+// split).  With M the largest m_s over non-empty splits (l_s > 0) and
+// w_s = 2^(m_s - M) (0 for empty splits):
+//   out = sum_s w_s O_s / sum_s w_s l_s, rounded to bf16 (ties to even).
+// One workgroup per (query, head).  Wave 0 reduces the nsplit (m, l) pairs
+// (one lane each); then thread i accumulates 4 dims over every G-th split
+// (G = 256 / (D/4) thread groups), and the G partial sums are added in group
+// order.  All sums have a fixed order: the result is deterministic.
+__global__ void __launch_bounds__(256)
+attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                    int nsplit, int H, int D, uint16_t* __restrict__ out) {
+  __shared__ float s_w[kMaxAttnSplits];
+  __shared__ float s_inv;
+  __shared__ f32x4_t s_acc[256];
+  const int tid = threadIdx.x;
+  const int64_t t = blockIdx.x;
+  const int h = blockIdx.y;
+  if (tid < 64) {
+    float m = -INFINITY, l = 0.f;
+    if (tid < nsplit) {
+      const float* ml = part_ml + ((t * nsplit + tid) * H + h) * 2;
+      m = ml[0];
+      l = ml[1];
+    }
+    const bool live = l > 0.f;
+    float M = live ? m : -INFINITY;
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float w = live ? exp2f(m - M) : 0.f;
+    float L = w * l;
+    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    if (tid < nsplit) s_w[tid] = w;
+    if (tid == 0) s_inv = L > 0.f ? 1.f / L : 0.f;
+  }
+  __syncthreads();
+  const int nd4 = D / 4;                 // 8 .. 128
+  const int G = 256 / nd4;               // thread groups over the splits
+  const int d4 = tid % nd4, g = tid / nd4;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const float* po = part_o + (t * nsplit * H + h) * static_cast<int64_t>(D) + 4 * d4;
+  const int64_t sstride = static_cast<int64_t>(H) * D;
+#pragma unroll 4
+  for (int sp = g; sp < nsplit; sp += G) {
+    const float w = s_w[sp];
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(po + sp * sstride);
+    acc += w * v;
+  }
+  s_acc[tid] = acc;
+  __syncthreads();
+  if (tid < nd4) {
+    f32x4_t sum = s_acc[tid];
+    for (int gg = 1; gg < G; ++gg) sum += s_acc[gg * nd4 + tid];
+    const float inv = s_inv;
+    uint16_t* op = out + (t * H + h) * static_cast<int64_t>(D) + 4 * tid;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) op[j] = bf16_rne(sum[j] * inv);
   }
 }
 
 }  // namespace
 
+hipError_t dsv4_launch_attn_combine(const float* part_o, const float* part_ml, int64_t T,
+                                    int32_t nsplit, int32_t n_heads, int32_t head_dim, void* out,
+                                    hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (nsplit > kMaxAttnSplits || head_dim % 4 != 0 || head_dim > 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<unsigned>(T), static_cast<unsigned>(n_heads)),
+                     dim3(256), 0, s, part_o, part_ml, nsplit, n_heads, head_dim,
+                     static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
 hipError_t dsv4_launch_sparse_attn(const void* q, int64_t T, int64_t q_pos0, int32_t n_heads,
                                    int32_t head_dim, float scale, const void* raw_kv,
                                    int64_t raw_pos0, int32_t window, const void* pooled,
                                    int32_t ratio, const int32_t* sel_idx, int32_t topk,
-                                   void* out, hipStream_t s) {
+                                   void* out, int32_t nsplit, float* part_o, float* part_ml,
+                                   hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  if (nsplit < 1) return hipErrorInvalidValue;
   const float sl2 = scale * 1.4426950408889634f;
   switch (head_dim) {
-    case 32: return launch_d<32>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, ratio, sel_idx, topk, out, s);
-    case 64: return launch_d<64>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, ratio, sel_idx, topk, out, s);
-    case 128: return launch_d<128>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, ratio, sel_idx, topk, out, s);
-    case 256: return launch_d<256>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, ratio, sel_idx, topk, out, s);
-    case 512: return launch_d<512>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, ratio, sel_idx, topk, out, s);
+    case 32: return launch_d<32>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, ratio, sel_idx, topk, out, nsplit, part_o, part_ml, s);
+    case 64: return launch_d<64>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, ratio, sel_idx, topk, out, nsplit, part_o, part_ml, s);
+    case 128: return launch_d<128>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, ratio, sel_idx, topk, out, nsplit, part_o, part_ml, s);
+    case 256: return launch_d<256>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, ratio, sel_idx, topk, out, nsplit, part_o, part_ml, s);
+    case 512: return launch_d<512>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, ratio, sel_idx, topk, out, nsplit, part_o, part_ml, s);
     default: return hipErrorInvalidValue;
   }
 }

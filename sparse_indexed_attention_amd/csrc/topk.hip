@@ -45,6 +45,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 2048;                    // 11-bit digits
 constexpr int kCandCap = 1024;                 // keys of one bin finished without more passes
 constexpr int kRankCap = 256;                  // ... by direct ranking (else bit by bit)
+constexpr int64_t kSplitChunk = 32 * kThreads; // columns of one single-chunk item
 
 // DPP move with 0 in lanes whose source is outside the pattern.
 template <int CTRL, int ROW_MASK>
@@ -101,15 +102,29 @@ struct Item {
   bool first, last;
 };
 
-// Work item `it` of workgroup g: rows g, g + G, ...; chunks of a row in order.
-template <int kChunk>
+// Work item `it` of workgroup g.  Normally rows g, g + G, ..., each row's
+// chunks in order (a tournament over them).  SPLIT (first pass of the
+// chunk-parallel top-k): items g, g + G, ... of the rows x chunks grid, each
+// chunk selected on its own into output row row * chunks_per_row + chunk.
+// A row's visible prefix is fixed_n columns when fixed_n >= 0 (second pass:
+// the candidate lists), else the causal prefix of its position.
+template <int kChunk, bool SPLIT>
 __device__ __forceinline__ bool item_of(int64_t it, int64_t rows, int64_t q_pos0, int64_t g,
-                                        int64_t G, int chunks_per_row, Item* o) {
-  const int64_t r_local = it / chunks_per_row;
-  const int ch = static_cast<int>(it - r_local * chunks_per_row);
-  const int64_t row = g + r_local * G;
+                                        int64_t G, int chunks_per_row, int64_t fixed_n,
+                                        Item* o) {
+  int64_t row;
+  int ch;
+  if (SPLIT) {
+    const int64_t id = g + it * G;
+    row = id / chunks_per_row;
+    ch = static_cast<int>(id - row * chunks_per_row);
+  } else {
+    const int64_t r_local = it / chunks_per_row;
+    ch = static_cast<int>(it - r_local * chunks_per_row);
+    row = g + r_local * G;
+  }
   if (row >= rows) return false;
-  const int64_t vis = visible_rows(q_pos0 + row);
+  const int64_t vis = fixed_n >= 0 ? fixed_n : visible_rows(q_pos0 + row);
   const int64_t base = static_cast<int64_t>(ch) * kChunk;
   o->row = row;
   o->base = base;
@@ -117,8 +132,8 @@ __device__ __forceinline__ bool item_of(int64_t it, int64_t rows, int64_t q_pos0
   if (n > kChunk) n = kChunk;
   if (n < 0) n = 0;
   o->n = static_cast<int>(n);
-  o->first = ch == 0;
-  o->last = (ch == chunks_per_row - 1) || (base + kChunk >= vis);
+  o->first = SPLIT || ch == 0;
+  o->last = SPLIT || (ch == chunks_per_row - 1) || (base + kChunk >= vis);
   return true;
 }
 
@@ -156,10 +171,26 @@ __device__ __forceinline__ void issue_item(const float* src, int n, float* buf, 
 // PER: columns per thread (chunk = PER * 1,024 columns).  DMA: rows start on
 // 16-byte boundaries, so items are copied with LDS DMA ahead of their use;
 // otherwise each item is loaded synchronously.
-template <int CPT, int PER, bool DMA>
+// Chunk-parallel top-k of a few long rows, in two passes over this kernel:
+//   SPLIT: every (row, chunk) item is selected on its own; output row
+//     row * chunks_per_row + chunk of out_idx gets the chunk's chosen
+//     columns (ascending, -1 padded) and the same row of cand_score their
+//     scores (-inf padded);
+//   then, with fixed_n = chunks_per_row * topk and remap = those columns:
+//     the top-k of each row's candidate scores, the chosen positions mapped
+//     back to columns through remap (same layout as the scores).
+// Exact: the top-k of a union under the total order (score desc, column
+// asc) is the top-k of the union of each part's top-k, and a row's
+// candidates lie in column order (chunks in order, each ascending, pads
+// last and never chosen while every row shows at least topk columns).
+enum TopkPass { kRows = 0, kSplit = 1, kMerge = 2 };
+
+template <int CPT, int PER, bool DMA, int PASS>
 __global__ void __launch_bounds__(kThreads)
 topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int64_t q_pos0,
-            int topk, int chunks_per_row, int32_t* __restrict__ out_idx) {
+            int topk, int chunks_per_row, int32_t* __restrict__ out_idx, int64_t fixed_n,
+            const int32_t* __restrict__ remap, float* __restrict__ cand_score) {
+  constexpr bool SPLIT = PASS == kSplit;
   constexpr int KMAX = CPT > 0 ? CPT * kThreads : 1;
   constexpr int kPer = PER;
   constexpr int kChunk = PER * kThreads;
@@ -179,11 +210,29 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
   uint32_t* const hist = work;
   uint32_t* const cand = work + kBins;
   int32_t* const obuf = kSepOut ? out_sep : reinterpret_cast<int32_t*>(work);
-  int64_t pend_row = -1;  // row whose staged output awaits its copy (kSepOut)
+  Item pend;  // item whose staged output awaits its copy (kSepOut)
+  bool have_pend = false;
   int pend_need = 0;
-  auto copy_out = [&](int64_t row, int nsel) {
-    int32_t* d = out_idx + row * static_cast<int64_t>(topk);
-    for (int j = static_cast<int>(threadIdx.x); j < topk; j += kThreads) d[j] = j < nsel ? obuf[j] : -1;
+  auto copy_out = [&](const Item& itm, int nsel) {
+    // output row: the row, or (row, chunk) in the chunk-parallel pass
+    const int64_t orow = SPLIT ? itm.row * chunks_per_row + itm.base / kChunk : itm.row;
+    int32_t* d = out_idx + orow * static_cast<int64_t>(topk);
+    if (SPLIT) {
+      float* ds = cand_score + orow * static_cast<int64_t>(topk);
+      const float* sr = scores + itm.row * stride;
+      for (int j = static_cast<int>(threadIdx.x); j < topk; j += kThreads) {
+        const int32_t col = j < nsel ? obuf[j] : -1;
+        d[j] = col;
+        ds[j] = col >= 0 ? sr[col] : -INFINITY;
+      }
+    } else if (PASS == kMerge) {
+      const int32_t* rm = remap + itm.row * stride;
+      for (int j = static_cast<int>(threadIdx.x); j < topk; j += kThreads)
+        d[j] = j < nsel ? rm[obuf[j]] : -1;
+    } else {
+      for (int j = static_cast<int>(threadIdx.x); j < topk; j += kThreads)
+        d[j] = j < nsel ? obuf[j] : -1;
+    }
   };
   __shared__ uint32_t scr[2][kWaves];
   __shared__ uint32_t s_red[4][kWaves];
@@ -199,7 +248,9 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
   uint32_t key[kPer];
   Item cur, nx;
   int64_t it = 0;
-  if (!item_of<kChunk>(it, rows, q_pos0, g, G, chunks_per_row, &cur)) return;
+  if (!item_of<kChunk, SPLIT>(it, rows, q_pos0, g, G, chunks_per_row,
+                              PASS == kMerge ? fixed_n : -1, &cur))
+    return;
   if (DMA) {
     issue_item(scores + cur.row * stride + cur.base, cur.n, rowbuf, wave, 0);
     issue_item(scores + cur.row * stride + cur.base, cur.n, rowbuf, wave, 1);
@@ -255,13 +306,15 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
       for (int i = tid; i < kBins; i += kThreads) hist[i] = 0u;
       if (tid == 0) s_ncand = 0u;
     }
-    const bool have_next = item_of<kChunk>(it + 1, rows, q_pos0, g, G, chunks_per_row, &nx);
+    const bool have_next =
+        item_of<kChunk, SPLIT>(it + 1, rows, q_pos0, g, G, chunks_per_row,
+                               PASS == kMerge ? fixed_n : -1, &nx);
     __syncthreads();  // every thread has its keys: the row buffer takes the next item
     if (DMA && have_next) issue_item(scores + nx.row * stride + nx.base, nx.n, rowbuf, wave, 0);
     bool second_half = DMA && have_next;  // the rest of the next item's copy, issued later
-    if (kSepOut && pend_row >= 0) {
-      copy_out(pend_row, pend_need);  // the previous item's staged row
-      pend_row = -1;
+    if (kSepOut && have_pend) {
+      copy_out(pend, pend_need);  // the previous item's staged row
+      have_pend = false;
     }
     if (cur.first) c = 0;
     // chunk slots past a shorter row's end carry no work (uniform branch)
@@ -562,16 +615,17 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
       // they are copied out coalesced and padded with -1 once every thread's
       // writes are in: after the next barrier (kSepOut: at the next item)
       if (kSepOut) {
-        pend_row = cur.row;
+        pend = cur;
+        have_pend = true;
         pend_need = need;
       } else {
         __syncthreads();
-        copy_out(cur.row, need);
+        copy_out(cur, need);
       }
     }
     __syncthreads();  // LDS tables / carry reused by the next item
     if (!have_next) {
-      if (kSepOut && pend_row >= 0) copy_out(pend_row, pend_need);
+      if (kSepOut && have_pend) copy_out(pend, pend_need);
       break;
     }
     cur = nx;
@@ -581,20 +635,41 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
 
 template <int CPT, int PER>
 hipError_t launch_cpt(const float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
-                      int32_t topk, int32_t* out_idx, hipStream_t s) {
+                      int32_t topk, int32_t* out_idx, int64_t fixed_n, const int32_t* remap,
+                      hipStream_t s) {
   const bool dma = (stride & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
-  const int64_t max_vis = (q_pos0 + rows) / 4;
+  const int64_t max_vis = fixed_n >= 0 ? fixed_n : (q_pos0 + rows) / 4;
   const int64_t chunk = static_cast<int64_t>(PER) * kThreads;
   const int chunks = static_cast<int>((max_vis + chunk - 1) / chunk);
   const int64_t G = rows < 256 ? rows : 256;  // one persistent workgroup per CU
   const int cpr = chunks > 0 ? chunks : 1;
-  if (dma)
-    hipLaunchKernelGGL((topk_kernel<CPT, PER, true>), dim3(static_cast<unsigned>(G)),
-                       dim3(kThreads), 0, s, scores, rows, stride, q_pos0, topk, cpr, out_idx);
-  else
-    hipLaunchKernelGGL((topk_kernel<CPT, PER, false>), dim3(static_cast<unsigned>(G)),
-                       dim3(kThreads), 0, s, scores, rows, stride, q_pos0, topk, cpr, out_idx);
+  if (remap) {  // merge pass: rows of candidate lists (no DMA: any stride)
+    hipLaunchKernelGGL((topk_kernel<CPT, PER, false, kMerge>), dim3(static_cast<unsigned>(G)),
+                       dim3(kThreads), 0, s, scores, rows, stride, q_pos0, topk, cpr, out_idx,
+                       fixed_n, remap, nullptr);
+  } else if (dma) {
+    hipLaunchKernelGGL((topk_kernel<CPT, PER, true, kRows>), dim3(static_cast<unsigned>(G)),
+                       dim3(kThreads), 0, s, scores, rows, stride, q_pos0, topk, cpr, out_idx,
+                       int64_t(-1), nullptr, nullptr);
+  } else {
+    hipLaunchKernelGGL((topk_kernel<CPT, PER, false, kRows>), dim3(static_cast<unsigned>(G)),
+                       dim3(kThreads), 0, s, scores, rows, stride, q_pos0, topk, cpr, out_idx,
+                       int64_t(-1), nullptr, nullptr);
+  }
   return hipGetLastError();
+}
+
+// Per-row top-k with the variant that fits the longest row: a single chunk,
+// or a tournament over chunks with the running top-k in LDS.
+hipError_t launch_rows(const float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
+                       int32_t topk, int32_t* out_idx, int64_t fixed_n, const int32_t* remap,
+                       hipStream_t s) {
+  const int64_t max_vis = fixed_n >= 0 ? fixed_n : (q_pos0 + rows) / 4;
+  if (max_vis <= kSplitChunk)
+    return launch_cpt<0, 32>(scores, rows, stride, q_pos0, topk, out_idx, fixed_n, remap, s);
+  if (topk <= 2048)
+    return launch_cpt<2, 32>(scores, rows, stride, q_pos0, topk, out_idx, fixed_n, remap, s);
+  return launch_cpt<4, 24>(scores, rows, stride, q_pos0, topk, out_idx, fixed_n, remap, s);
 }
 
 }  // namespace
@@ -602,8 +677,36 @@ hipError_t launch_cpt(const float* scores, int64_t rows, int64_t stride, int64_t
 hipError_t dsv4_launch_topk(const float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
                             int32_t topk, int32_t* out_idx, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  return launch_rows(scores, rows, stride, q_pos0, topk, out_idx, -1, nullptr, s);
+}
+
+int64_t dsv4_topk_split_chunks(int64_t rows, int64_t q_pos0) {
   const int64_t max_vis = (q_pos0 + rows) / 4;
-  if (max_vis <= 32 * kThreads) return launch_cpt<0, 32>(scores, rows, stride, q_pos0, topk, out_idx, s);
-  if (topk <= 2048) return launch_cpt<2, 32>(scores, rows, stride, q_pos0, topk, out_idx, s);
-  return launch_cpt<4, 24>(scores, rows, stride, q_pos0, topk, out_idx, s);
+  return (max_vis + kSplitChunk - 1) / kSplitChunk;
+}
+
+hipError_t dsv4_launch_topk_split(const float* scores, int64_t rows, int64_t stride,
+                                  int64_t q_pos0, int32_t topk, int32_t* out_idx,
+                                  int32_t* cand_idx, float* cand_score, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t cpr = dsv4_topk_split_chunks(rows, q_pos0);
+  if (cpr < 1 || cpr * topk > (int64_t(1) << 30)) return hipErrorInvalidValue;
+  // pass 1: every (row, chunk) item on its own, as many workgroups as items
+  // (at most one per CU, persistent)
+  const int64_t items = rows * cpr;
+  const int64_t G = items < 256 ? items : 256;
+  const bool dma = (stride & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
+  if (dma)
+    hipLaunchKernelGGL((topk_kernel<0, 32, true, kSplit>), dim3(static_cast<unsigned>(G)),
+                       dim3(kThreads), 0, s, scores, rows, stride, q_pos0, topk,
+                       static_cast<int>(cpr), cand_idx, int64_t(-1), nullptr, cand_score);
+  else
+    hipLaunchKernelGGL((topk_kernel<0, 32, false, kSplit>), dim3(static_cast<unsigned>(G)),
+                       dim3(kThreads), 0, s, scores, rows, stride, q_pos0, topk,
+                       static_cast<int>(cpr), cand_idx, int64_t(-1), nullptr, cand_score);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // pass 2: top-k of each row's cpr * topk candidates, mapped back to columns
+  const int64_t n2 = cpr * topk;
+  return launch_rows(cand_score, rows, n2, q_pos0, topk, out_idx, n2, cand_idx, s);
 }

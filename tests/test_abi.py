@@ -23,7 +23,7 @@ def test_library_exports_every_header_function():
 
 
 def test_abi_version_and_host_helpers():
-    assert dsv4.dsv4_abi_version() == 2
+    assert dsv4.dsv4_abi_version() == 3
     assert dsv4.dsv4_indexer_all_pooled(0, 8) is False
     assert dsv4.dsv4_indexer_all_pooled(1, 8) is True
     assert dsv4.dsv4_indexer_all_pooled(8, 8) is True
@@ -143,3 +143,52 @@ def test_attention_gates():
     assert _rc("dsv4_sparse_prefill_attn", ctypes.c_void_p(FAKE), 4, 100, 64, 96, 0.0,
                ctypes.c_void_p(FAKE), 0, 104, 128, None, None, 0,
                ctypes.c_void_p(FAKE), None) == UNSUPPORTED
+
+
+def test_narrow_attention_plan_and_gates():
+    ns, nb = dsv4.dsv4_sparse_attn_narrow_plan(1, 64, 512, 128, 2048)
+    assert ns == 34 and nb == 1 * 34 * 64 * (512 + 2) * 4     # 68 tiles, 2 per split
+    assert dsv4.dsv4_sparse_attn_narrow_plan(4, 64, 512, 128, 2048)[0] == 34
+    assert dsv4.dsv4_sparse_attn_narrow_plan(64, 64, 512, 128, 2048)[0] == 4   # 256 / 64
+    assert dsv4.dsv4_sparse_attn_narrow_plan(1, 64, 512, 128, 0) == (2, 2 * 64 * 514 * 4)
+    assert dsv4.dsv4_sparse_attn_narrow_plan(300, 64, 512, 128, 2048) == (1, 0)
+    assert dsv4.dsv4_sparse_attn_narrow_plan(1, 64, 512, 128, 10 ** 6)[0] == 64  # cap
+    with pytest.raises(dsv4.DSV4Error):
+        dsv4.dsv4_sparse_attn_narrow_plan(1, 0, 512, 128, 0)
+    c = _cache(n_rows=40, dim=512, cap=64)
+
+    def call(n_splits=4, ws=FAKE, nbytes=1 << 30, sel=FAKE, T=4):
+        return _rc("dsv4_sparse_attn_narrow", ctypes.c_void_p(FAKE), T, 100, 64, 512, 0.0,
+                   ctypes.c_void_p(FAKE), 0, 104, 128, ctypes.byref(c), ctypes.c_void_p(sel), 16,
+                   n_splits, ctypes.c_void_p(ws) if ws else None, nbytes,
+                   ctypes.c_void_p(FAKE), None)
+    assert call(n_splits=0) == UNSUPPORTED
+    assert call(n_splits=65) == UNSUPPORTED
+    assert call(ws=0) == INVALID
+    assert call(ws=FAKE + 4) == INVALID                       # not 16-byte aligned
+    assert call(nbytes=4 * 4 * 64 * 514 * 4 - 1) == SCRATCH   # one byte short
+    assert "workspace" in dsv4.dsv4_last_error()
+    assert call(T=0, n_splits=4, ws=0) == OK                  # nothing to do
+
+
+def test_split_topk_sizing_and_gates():
+    ws = dsv4.dsv4_topk_split_workspace_bytes
+    # 1 row at position 2^20 - 4: 262,143 visible -> 8 chunks of 32,768
+    assert ws(1, (1 << 20) - 4, 2048) == 2 * 8 * 2048 * 4
+    assert ws(3, (1 << 20) - 4, 7) == 2 * ((3 * 8 * 7 * 4 + 15) // 16 * 16)
+    assert ws(65, (1 << 20) - 4, 2048) == 0           # too many rows: per-row kernel
+    assert ws(1, 4 * 32767, 2048) == 0                # one chunk
+    # narrow tiles over long rows get room for the split top-k (sized for k = 4096)
+    assert dsv4.dsv4_indexer_scratch_bytes(1, 262144) == 262144 * 4 + 2 * 8 * 4096 * 4
+    assert dsv4.dsv4_indexer_scratch_bytes(64, 32768) == 64 * 32768 * 4
+    assert dsv4.dsv4_indexer_scratch_bytes(65, 262144) == 65 * 262144 * 4
+
+    def call(ws_ptr, nbytes, rows=2, q_pos0=(1 << 20) - 8):
+        return _rc("dsv4_topk_select_split", ctypes.c_void_p(FAKE), rows, 262144, q_pos0, 262144,
+                   2048, ctypes.c_void_p(FAKE), ctypes.c_void_p(ws_ptr) if ws_ptr else None,
+                   nbytes, None)
+    assert call(0, 0) == INVALID
+    assert call(FAKE + 8, 1 << 20) == INVALID                 # misaligned
+    assert call(FAKE, 2 * 2 * 8 * 2048 * 4 - 16) == SCRATCH
+    assert "workspace" in dsv4.dsv4_last_error()
+    assert call(FAKE, 1 << 20, q_pos0=(1 << 20) + 4) == INVALID   # sees past 262,144 columns
