@@ -341,13 +341,15 @@ hipError_t launch_t(const void* q, const float* w, const void* keys, int64_t row
   const int cgroups = nqb >= 16 ? 4 : 8;
   const int64_t qgroups = 8 / cgroups;
   const int64_t nqb_g = (nqb + qgroups - 1) / qgroups;  // query blocks per query group
-  // Column splits per column group.  About two workgroups per CU in total
-  // (512) for narrow query counts, four (1,024) from 32 query blocks up:
-  // every workgroup re-reads its queries and runs a pipeline prologue, so
-  // more, shorter splits lose (at 64 query rows, 4,096 one-tile splits take
-  // twice as long as 256 long ones), while fewer than one round over the
-  // CUs leaves the chip idle.  At least one tile per split.
-  const int64_t target_wg = nqb >= 32 ? 1024 : 512;
+  // Column splits per column group.  Every workgroup re-reads its queries
+  // and runs a pipeline prologue, so for few query blocks more, shorter
+  // splits lose (at 64 query rows, 4,096 one-tile splits take twice as long
+  // as 256 long ones): about two workgroups per CU in all (512) below 32
+  // query blocks, four (1,024) below 128.  From 128 blocks (1,024 rows) the
+  // splits are long anyway and 4,096 workgroups keep the key ranges that
+  // share an XCD's L2 narrowest (least HBM fetch at equal time).  At least
+  // one tile per split.
+  const int64_t target_wg = nqb >= 128 ? 4096 : (nqb >= 32 ? 1024 : 512);
   int64_t per_cg = (target_wg + 8 * nqb_g - 1) / (8 * nqb_g);
   int64_t max_per_cg = S / (static_cast<int64_t>(cgroups) * kTileCols);
   if (max_per_cg < 1) max_per_cg = 1;
