@@ -138,3 +138,80 @@ def test_ctx16k_eight_chunks_skip_then_full():
                 assert_selection_matches(gidx[t:t + 1], ref, q_pos0 + t, k)
     np.testing.assert_array_equal(icache.rows[:icache.n_rows].float().cpu().numpy(),
                                   ost.rows[:ost.n_rows])
+
+
+# ---------------------------------------------------------------- sibling modes and narrow steps
+# The same launch configurations bench.py times: the 2,048-row chunk at 128K
+# context in the window-only and ratio-128 modes, and T = 1-4 query rows at
+# the end of a context.
+
+def test_ctx128k_chunk2048_local_and_ratio128_modes():
+    wl = SI.CTX_128K
+    cs = ChunkState(wl)
+    T, H, D, W = wl.chunk, wl.heads, wl.head_dim, wl.window
+    scale = 1 / math.sqrt(D)
+    rows = sample_rows(T, T, 6, seed=3)
+    # window only
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    dsv4.dsv4_sparse_prefill_attn(cs.q_attn, cs.q_pos0, cs.raw_kv, cs.raw_pos0, W, None, None, out)
+    torch.cuda.synchronize()
+    g = out[rows].float().cpu().numpy()
+    for i, t in enumerate(rows):
+        ref = O.sparse_prefill_attention(cs.inp["q_attn"][t:t + 1], cs.q_pos0 + t, cs.inp["raw_kv"],
+                                         cs.raw_pos0, W, None, None, scale)
+        assert np.abs(g[i] - ref[0]).max() <= ATTN_ATOL, ("local", t)
+    # ratio-128 pool: prefix rows, then the chunk through the compressor
+    prefix_t, prefix = SI.prefix_rows_ratio(wl, 0, 128)
+    n128 = prefix.shape[0]
+    c128 = dsv4.PoolCache(n128 + T // 128 + 1, D, ratio=128)
+    c128.rows[:n128].copy_(prefix_t)
+    c128.set_state(n128, 0)
+    chunk = cs.inp["raw_kv"][cs.q_pos0 - cs.raw_pos0:]
+    dsv4.dsv4_compress(c128, cs.raw_kv[cs.q_pos0 - cs.raw_pos0:])
+    st = O.PoolingCacheState(D, n128 + T // 128 + 1, ratio=128)
+    st.rows[:n128] = prefix
+    st.n_rows = n128
+    O.compress(st, chunk)
+    S = c128.n_rows
+    assert S == st.n_rows == (cs.q_pos0 + T) // 128
+    dsv4.dsv4_sparse_prefill_attn(cs.q_attn, cs.q_pos0, cs.raw_kv, cs.raw_pos0, W, c128, None, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(c128.rows[n128:S].float().cpu().numpy(), st.rows[n128:S])
+    g = out[rows].float().cpu().numpy()
+    for i, t in enumerate(rows):
+        ref = O.sparse_prefill_attention(cs.inp["q_attn"][t:t + 1], cs.q_pos0 + t, cs.inp["raw_kv"],
+                                         cs.raw_pos0, W, st.rows[:S], None, scale, ratio=128)
+        assert np.abs(g[i] - ref[0]).max() <= ATTN_ATOL, ("ratio128", t)
+
+
+@pytest.mark.parametrize("wl,T", [(SI.CTX_128K, 4), (SI.CTX_1M, 2)], ids=["ctx128k-T4", "ctx1m-T2"])
+def test_narrow_steps_at_end_of_context(wl, T):
+    """T query rows at the last positions the caches cover, as bench.py's
+    narrow section runs them: indexer select with the scratch
+    dsv4_indexer_scratch_bytes sizes (the chunk-parallel top-k at 1M), then
+    the key-split attention with its planned split count.  Every row is
+    checked."""
+    cs = ChunkState(wl)
+    S = cs.S
+    H, D, W, k = wl.heads, wl.head_dim, wl.window, wl.topk
+    q0 = 4 * S - T
+    scratch = torch.empty(dsv4.dsv4_indexer_scratch_bytes(T, S) // 4, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    assert not dsv4.dsv4_indexer_select(cs.icache, cs.acache.n_rows, cs.q_idx[:T], cs.w[:T], T, q0,
+                                        wl.idx_heads, k, idx, scratch, 0)
+    ns, nb = dsv4.dsv4_sparse_attn_narrow_plan(T, H, D, W, k)
+    assert ns > 1
+    ws = torch.empty(nb // 4, device="cuda")
+    raw_lo = q0 - W + 1
+    raw = cs.raw_kv[raw_lo - cs.raw_pos0:q0 + T - cs.raw_pos0]
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    dsv4.dsv4_sparse_attn_narrow(cs.q_attn[:T], q0, raw, raw_lo, W, cs.acache, idx, out, ns, ws)
+    torch.cuda.synchronize()
+    gidx = idx.cpu().numpy()
+    ref = O.indexer_scores(cs.inp["q_idx"][:T], cs.inp["w"][:T], cs.oracle_keys(), q0, S)
+    assert_selection_matches(gidx, ref, q0, k)
+    raw_np = cs.inp["raw_kv"][raw_lo - cs.raw_pos0:q0 + T - cs.raw_pos0]
+    ref_o = O.sparse_prefill_attention(cs.inp["q_attn"][:T], q0, raw_np, raw_lo, W,
+                                       cs.oracle_pooled(), gidx, 1 / math.sqrt(D))
+    err = np.abs(out.float().cpu().numpy() - ref_o).max()
+    assert err <= ATTN_ATOL, err
