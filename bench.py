@@ -230,6 +230,46 @@ def timed_kernel(fn, reps: int) -> float:
     return a.elapsed_time(b) / reps
 
 
+def per_call_stats(fn, reps: int, scrub=None) -> dict:
+    """Median and min ms of single calls of fn(), each bracketed by its own HIP
+    events on the current stream.  With `scrub` (a large tensor), the buffer
+    is overwritten before every call so the call starts with cold caches
+    (the 256 MB MALL and the L2s hold none of its inputs)."""
+    fn()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        if scrub is not None:
+            scrub.fill_(float(len(times) + 1))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    return {"median": float(np.median(times)), "min": float(np.min(times))}
+
+
+def achievable_peaks() -> dict:
+    """What this machine reaches with plain library work in the same process: a
+    1 GiB device-to-device copy (2 GiB moved) and a 8192^3 bf16 GEMM
+    (torch.matmul on contiguous operands).  Reported beside the spec peaks."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ms_copy = timed_kernel(lambda: dst.copy_(src), 10)
+    del src, dst
+    m = 8192
+    a = torch.randn((m, m), device="cuda").to(torch.bfloat16)
+    b = torch.randn((m, m), device="cuda").to(torch.bfloat16)
+    ms_gemm = timed_kernel(lambda: torch.matmul(a, b), 10)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBps": 2 * n * 4 / (ms_copy * 1e-3) / 1e9,
+            "bf16_gemm_TFLOPs": 2 * m ** 3 / (ms_gemm * 1e-3) / 1e12,
+            "how": "1 GiB device copy; 8192^3 bf16 torch.matmul (hipBLASLt), same process"}
+
+
 def measure_modes(setup: Setup, reps: int) -> dict:
     """The sibling attention modes of the same fused kernel on this chunk:
     window-only (LocalAttention) and window + every visible ratio-128 pooled
@@ -493,7 +533,25 @@ def main():
                      * (min(wl.window, p + 1) + min(wl.topk, (p + 1) // 4))
                      for p in range(wl.q_pos0, wl.q_pos0 + T))
     attn_tflops = attn_flops / (attn * 1e-3) / 1e12
+    attn_gather = sum(2 * wl.head_dim * (min(wl.window, p + 1) + min(wl.topk, (p + 1) // 4))
+                      for p in range(wl.q_pos0, wl.q_pos0 + T))
 
+    # per-call median / min, warm and cold (a 512 MiB write between calls)
+    sel_fn = lambda: d.dsv4_indexer_select(setup.icache, setup.acache.n_rows, setup.q_idx, setup.w,
+                                           T, wl.q_pos0, wl.idx_heads, wl.topk, setup.idx,
+                                           setup.scratch, wl.tile_rows)
+    attn_fn = lambda: d.dsv4_sparse_prefill_attn(setup.q_attn, wl.q_pos0, setup.raw_kv,
+                                                 setup.raw_pos0, wl.window, setup.acache,
+                                                 setup.idx, setup.out)
+    reps = max(5, args.steps // 2)
+    scrub = torch.empty(512 << 18, dtype=torch.float32, device="cuda")
+    calls = {"indexer_select": {"warm": per_call_stats(sel_fn, reps),
+                                "cold": per_call_stats(sel_fn, reps, scrub)},
+             "attention": {"warm": per_call_stats(attn_fn, reps),
+                           "cold": per_call_stats(attn_fn, reps, scrub)}}
+    del scrub
+    torch.cuda.empty_cache()
+    peaks = achievable_peaks()
     modes = measure_modes(setup, max(5, args.steps // 2)) if not args.no_modes else None
     narrow = measure_narrow(setup, max(10, args.steps)) if not args.no_modes else None
     cpu = cpu_baseline(setup, args.cpu_seconds) if args.cpu_seconds > 0 else None
@@ -522,11 +580,17 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "indexer_score", "achieved": score_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": score_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": recorded_traffic(wl.name)},
+                     "traffic": recorded_traffic(wl.name),
+                     "frac_of_achievable": score_tflops / peaks["bf16_gemm_TFLOPs"]},
+        "per_call_ms": calls,
+        "achievable": peaks,
         "topk_roofline": {"bound": "hbm", "achieved": topk_gbs, "peak": PEAK_HBM_GBS,
-                          "unit": "GB/s", "frac": topk_gbs / PEAK_HBM_GBS},
+                          "unit": "GB/s", "frac": topk_gbs / PEAK_HBM_GBS,
+                          "frac_of_achievable": topk_gbs / peaks["hbm_copy_GBps"]},
         "attn_roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
-                          "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS},
+                          "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
+                          "frac_of_achievable": attn_tflops / peaks["bf16_gemm_TFLOPs"],
+                          "gather_GBps": attn_gather / (attn * 1e-3) / 1e9},
         "modes": modes,
         "narrow": narrow,
         "cpu_baseline": cpu,
