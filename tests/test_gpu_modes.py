@@ -180,3 +180,53 @@ def test_compressed_attention_end_to_end_after_ratio128_compress():
                                      1 / math.sqrt(D), ratio=128)
     err = np.abs(out.float().cpu().numpy() - ref).max()
     assert err <= ATTN_ATOL, err
+
+
+# ====================================================================== maximum sizes
+
+def test_attention_at_maximum_topk():
+    """top-k = DSV4_MAX_TOPK (4,096: the largest selection row the kernels hold
+    in LDS) with H = 64, D = 512, through both attention entry points."""
+    T, q_pos0, H, D, W, topk = 5, 4 * 6000, 64, 512, 128, 4096
+    rng = np.random.default_rng(4096)
+    raw_pos0 = q_pos0 - W + 1
+    q, raw = _rand_q_raw(rng, T, q_pos0, H, D, raw_pos0)
+    S = (q_pos0 + T) // 4
+    pooled = SI.as_bf16_values(rng.standard_normal((S, D)).astype(np.float32) * 0.5)
+    cache = dsv4.PoolCache(S, D)
+    cache.rows.copy_(bf16_t(pooled))
+    cache.set_state(S, (q_pos0 + T) - 4 * S)
+    sel = np.full((T, topk), -1, np.int32)
+    for t in range(T):
+        v = (q_pos0 + t + 1) // 4
+        sel[t] = np.sort(rng.choice(v, size=topk, replace=False))
+    sel[2, topk - 1] = -1       # an empty last slot
+    ref = O.sparse_prefill_attention(q, q_pos0, raw, raw_pos0, W, pooled, sel, 1 / math.sqrt(D))
+    seld = torch.from_numpy(sel).cuda()
+    a = _run(q, q_pos0, raw, raw_pos0, W, cache, seld)
+    ns, nb = dsv4.dsv4_sparse_attn_narrow_plan(T, H, D, W, topk)
+    ws = torch.empty(nb // 4, dtype=torch.float32, device="cuda")
+    b = torch.zeros((T, H, D), dtype=torch.bfloat16, device="cuda")
+    dsv4.dsv4_sparse_attn_narrow(bf16_t(q.reshape(T, H * D)).cuda().view(T, H, D), q_pos0,
+                                 bf16_t(raw).cuda(), raw_pos0, W, cache, seld, b, ns, ws)
+    torch.cuda.synchronize()
+    assert np.abs(a.float().cpu().numpy() - ref).max() <= ATTN_ATOL
+    assert np.abs(b.float().cpu().numpy() - ref).max() <= ATTN_ATOL
+
+
+def test_compress_at_maximum_ratio_is_bit_exact():
+    # ratio 256 (DSV4_MAX_RATIO): 2 rows + a 255-row remainder, then one more token
+    rng = np.random.default_rng(256)
+    n, dim = 256 * 3 - 1, 64
+    x = SI.as_bf16_values(rng.standard_normal((n + 1, dim)).astype(np.float32))
+    ref = O.PoolingCacheState(dim, 4, ratio=256)
+    c = dsv4.PoolCache(4, dim, ratio=256)
+    xd = bf16_t(x).cuda()
+    O.compress(ref, x[:n])
+    dsv4.dsv4_compress(c, xd[:n])
+    assert (c.n_rows, c.n_rem) == (ref.n_rows, ref.n_rem) == (2, 255)
+    O.compress(ref, x[n:])
+    dsv4.dsv4_compress(c, xd[n:])
+    torch.cuda.synchronize()
+    assert (c.n_rows, c.n_rem) == (ref.n_rows, ref.n_rem) == (3, 0)
+    np.testing.assert_array_equal(c.rows[:3].float().cpu().numpy(), ref.rows[:3])
