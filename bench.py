@@ -313,7 +313,8 @@ def measure_narrow(setup: Setup, reps: int) -> dict:
     short prefill bands) at the end of this workload's context, against the
     same caches: the indexer select (scratch as dsv4_indexer_scratch_bytes
     sizes it) and the key-split attention with its planned split count.
-    HIP-event means over `reps` calls of each."""
+    HIP-event means over `reps` calls of each, eager and as a replayed HIP
+    graph of the whole step."""
     d, wl = setup.dsv4, setup.wl
     S = setup.S_after
     H, D, W, k = wl.heads, wl.head_dim, wl.window, wl.topk
@@ -339,8 +340,23 @@ def measure_narrow(setup: Setup, reps: int) -> dict:
         ms_sel = timed_kernel(sel, reps)
         ms_attn = timed_kernel(attn, reps)
         ms_step = timed_kernel(lambda: (sel(), attn()), reps)
+        # the same step captured once in a HIP graph and replayed (no host
+        # launch work per kernel)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            sel(); attn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            sel(); attn()
+        torch.cuda.synchronize()
+        ms_graph = timed_kernel(graph.replay, reps)
         res[f"T{T}"] = {"select_ms": ms_sel, "attention_ms": ms_attn, "attention_splits": ns,
-                        "step_ms": ms_step, "query_rows_per_s": T / (ms_step * 1e-3)}
+                        "step_ms": ms_step, "query_rows_per_s": T / (ms_step * 1e-3),
+                        "graph_step_ms": ms_graph,
+                        "graph_query_rows_per_s": T / (ms_graph * 1e-3)}
     return res
 
 
