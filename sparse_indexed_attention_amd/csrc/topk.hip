@@ -539,6 +539,12 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
       T = prefix;
       need_eq = remaining;
     }
+    // every path issues the rest of the next item's copy before the emission
+    // (an item whose keys are all equal skips the histogram loop above)
+    if (second_half) {
+      issue_item(scores + nx.row * stride + nx.base, nx.n, rowbuf, wave, 1);
+      second_half = false;
+    }
 
     // ---- ordered emission: carry entries first, then the chunk, thread order
     uint32_t c_gt = 0, c_eq = 0;

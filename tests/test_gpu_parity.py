@@ -359,3 +359,19 @@ def test_tiny_workload_end_to_end():
                                      wl.window, cs.oracle_pooled(), gsel,
                                      1 / math.sqrt(wl.head_dim))
     assert np.abs(attn.float().cpu().numpy() - ref).max() <= ATTN_ATOL
+
+
+def test_topk_constant_rows_between_ordinary_rows():
+    """A row whose visible scores are all equal (a zero query or zero head
+    weights give such a row of zeros) followed, in the same persistent
+    workgroup, by ordinary rows longer than 4,096 columns: every row must
+    still be the oracle's selection (each workgroup takes rows g, g + 256, ...
+    of a 2,048-row tile)."""
+    rng = np.random.default_rng(44)
+    rows, q_pos0, topk = 1024, 4 * 30000, 2048
+    n_cols = (q_pos0 + rows) // 4
+    s = rng.standard_normal((rows, n_cols)).astype(np.float32)
+    s[::3] = 0.0                       # every third row constant (ties everywhere)
+    s[1::7] = np.float32(-2.5)
+    got = _topk_gpu(s, q_pos0, n_cols, topk)
+    np.testing.assert_array_equal(got, O.topk_select(s.astype(np.float64), q_pos0, topk))
