@@ -375,3 +375,17 @@ def test_topk_constant_rows_between_ordinary_rows():
     s[1::7] = np.float32(-2.5)
     got = _topk_gpu(s, q_pos0, n_cols, topk)
     np.testing.assert_array_equal(got, O.topk_select(s.astype(np.float64), q_pos0, topk))
+
+
+@pytest.mark.parametrize("levels", [40, 10, 3])
+def test_topk_tie_heavy_long_rows(levels):
+    """Single-chunk rows of 30,000 columns holding only `levels` distinct
+    values: the threshold bin holds ~30,000/levels keys, so the finish takes
+    the one-wave bit-by-bit path (40 levels) or further histogram passes
+    (10, 3); several rows share each persistent workgroup."""
+    rng = np.random.default_rng(levels)
+    rows, q_pos0, topk = 600, 4 * 30000, 2048
+    n_cols = (q_pos0 + rows) // 4
+    s = rng.integers(0, levels, size=(rows, n_cols)).astype(np.float32) - levels / 2
+    got = _topk_gpu(s, q_pos0, n_cols, topk)
+    np.testing.assert_array_equal(got, O.topk_select(s.astype(np.float64), q_pos0, topk))
