@@ -389,3 +389,21 @@ def test_topk_tie_heavy_long_rows(levels):
     s = rng.integers(0, levels, size=(rows, n_cols)).astype(np.float32) - levels / 2
     got = _topk_gpu(s, q_pos0, n_cols, topk)
     np.testing.assert_array_equal(got, O.topk_select(s.astype(np.float64), q_pos0, topk))
+
+
+def test_attention_unsorted_and_duplicate_selections():
+    """Selections the indexer never makes but the ABI accepts: slots in
+    descending order and repeated rows.  Each listed slot is a key, as in the
+    definition (a row listed twice is attended twice)."""
+    T, q_pos0, H, D, W, topk = 12, 2000, 64, 512, 128, 96
+    cache, pooled, raw, raw_pos0, q, sel = _attn_case(T, q_pos0, H, D, W, topk, seed=77)
+    sel = sel[:, ::-1].copy()                 # descending, -1 slots first
+    sel[:, 5] = sel[:, 6]                     # a repeated row in every query
+    sel[3, :] = sel[3, 7]                     # one query: a single row, topk times
+    out = torch.zeros((T, H, D), dtype=torch.bfloat16, device="cuda")
+    dsv4.dsv4_sparse_prefill_attn(bf16_t(q.reshape(T, H * D)).cuda().view(T, H, D), q_pos0,
+                                  bf16_t(raw).cuda(), raw_pos0, W, cache,
+                                  torch.from_numpy(sel).cuda(), out)
+    torch.cuda.synchronize()
+    ref = O.sparse_prefill_attention(q, q_pos0, raw, raw_pos0, W, pooled, sel, 1 / math.sqrt(D))
+    assert np.abs(out.float().cpu().numpy() - ref).max() <= ATTN_ATOL
