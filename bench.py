@@ -149,6 +149,8 @@ def parse():
     ap.add_argument("--matrix", action="store_true",
                     help="instead of the benchmark, time the (global chunk, indexer tile) matrix "
                          "at 1M context, serial and ping-pong, one JSON line per pair")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="one bench line per named workload (tiny .. 1M), without the extras")
     ap.add_argument("--no-modes", action="store_true",
                     help="skip the sibling-mode and narrow-query measurements")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -505,7 +507,30 @@ def main():
     if args.matrix:
         tile_matrix(max(3, args.steps // 4))
         return
-    wl = SI.WORKLOADS[args.workload]
+    if args.all_configs:
+        # one line per named workload (the headline line is the default run)
+        for name in ("tiny-64tok", "ctx4k-chunk2048", "ctx16k-chunk2048", "ctx128k-chunk2048",
+                     "ctx1m-chunk4096-tile1024"):
+            rec = run_workload(args, SI.WORKLOADS[name], extras=False)
+            print(json.dumps(rec))
+            sys.stdout.flush()
+            torch.cuda.empty_cache()
+        return
+    rec = run_workload(args, SI.WORKLOADS[args.workload], extras=True)
+    print(json.dumps(rec))
+    sys.stdout.flush()
+    if args.calibration_copy:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)  # elementwise kernel: reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+
+
+def run_workload(args, wl: SI.Workload, extras: bool) -> dict:
+    """Warmup, the timed steps and the per-kernel measurements of one
+    workload; `extras` adds the per-call, achievable-peak, sibling-mode and
+    narrow-step measurements."""
     setup = Setup(wl, args.seed)
     d = setup.dsv4
     T = wl.chunk
@@ -560,17 +585,22 @@ def main():
                                                  setup.raw_pos0, wl.window, setup.acache,
                                                  setup.idx, setup.out)
     reps = max(5, args.steps // 2)
-    scrub = torch.empty(512 << 18, dtype=torch.float32, device="cuda")
-    calls = {"indexer_select": {"warm": per_call_stats(sel_fn, reps),
-                                "cold": per_call_stats(sel_fn, reps, scrub)},
-             "attention": {"warm": per_call_stats(attn_fn, reps),
-                           "cold": per_call_stats(attn_fn, reps, scrub)}}
-    del scrub
-    torch.cuda.empty_cache()
-    peaks = achievable_peaks()
-    modes = measure_modes(setup, max(5, args.steps // 2)) if not args.no_modes else None
-    narrow = measure_narrow(setup, max(10, args.steps)) if not args.no_modes else None
-    cpu = cpu_baseline(setup, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    calls = peaks = modes = narrow = None
+    if extras:
+        scrub = torch.empty(512 << 18, dtype=torch.float32, device="cuda")
+        calls = {"indexer_select": {"warm": per_call_stats(sel_fn, reps),
+                                    "cold": per_call_stats(sel_fn, reps, scrub)},
+                 "attention": {"warm": per_call_stats(attn_fn, reps),
+                               "cold": per_call_stats(attn_fn, reps, scrub)}}
+        del scrub
+        torch.cuda.empty_cache()
+        peaks = achievable_peaks()
+        if not args.no_modes:
+            modes = measure_modes(setup, max(5, args.steps // 2))
+            narrow = measure_narrow(setup, max(10, args.steps))
+    budget = args.cpu_seconds if extras else min(args.cpu_seconds, 4.0)
+    cpu = cpu_baseline(setup, budget) if budget > 0 else None
+    ach = (lambda x, key: x / peaks[key]) if peaks else (lambda x, key: None)
     rec = {
         "metric": "indexer score+top-k query rows/s and pooled-row scores/s at 128K ctx; MFMA util",
         "value": T / (sel * 1e-3),
@@ -597,28 +627,21 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": score_tflops / PEAK_BF16_TFLOPS,
                      "traffic": recorded_traffic(wl.name),
-                     "frac_of_achievable": score_tflops / peaks["bf16_gemm_TFLOPs"]},
+                     "frac_of_achievable": ach(score_tflops, "bf16_gemm_TFLOPs")},
         "per_call_ms": calls,
         "achievable": peaks,
         "topk_roofline": {"bound": "hbm", "achieved": topk_gbs, "peak": PEAK_HBM_GBS,
                           "unit": "GB/s", "frac": topk_gbs / PEAK_HBM_GBS,
-                          "frac_of_achievable": topk_gbs / peaks["hbm_copy_GBps"]},
+                          "frac_of_achievable": ach(topk_gbs, "hbm_copy_GBps")},
         "attn_roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                           "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                          "frac_of_achievable": attn_tflops / peaks["bf16_gemm_TFLOPs"],
+                          "frac_of_achievable": ach(attn_tflops, "bf16_gemm_TFLOPs"),
                           "gather_GBps": attn_gather / (attn * 1e-3) / 1e9},
         "modes": modes,
         "narrow": narrow,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(rec))
-    sys.stdout.flush()
-    if args.calibration_copy:
-        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)  # elementwise kernel: reads 1 GiB, writes 1 GiB
-        torch.cuda.synchronize()
+    return rec
 
 
 if __name__ == "__main__":
