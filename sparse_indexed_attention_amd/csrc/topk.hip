@@ -639,6 +639,371 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
   }
 }
 
+// ---------------------------------------------------------------------------
+// Short rows (at most 64 * KPL visible columns): one wave per row, no
+// workgroup barriers.  The same selection rule as above, laid out for rows
+// that one wave can hold in registers:
+//   * lane L holds the float4 at columns 256v + 4L .. 256v + 4L + 3 for
+//     v = 0 .. KPL/4 - 1 (each load instruction reads 1 KiB contiguous), as
+//     keys key[4v + i]; columns past the visible prefix get key 0, and only
+//     the steps v that reach past it test for that (a wave-uniform branch);
+//   * threshold: MSB-first radix select with 11-bit digits over a 2,048-bin
+//     LDS histogram private to the wave, from the highest bit in which the
+//     row's keys differ (wave OR of the keys and of their complements); once
+//     the bin holding the k-th key has at most 64 keys they are listed, one
+//     per lane, and ballot counts settle the remaining bits one at a time;
+//   * list building and ordered emission give each key its place with one
+//     packed wave scan per three steps (10-bit per-step counts), and every
+//     key makes one unconditional LDS write, to its slot or to a slot of its
+//     own lane that is never read (no per-key branches).  When every key
+//     equal to the threshold T is chosen (the usual case) the choice is
+//     simply key >= T; otherwise equal keys go to the lower columns.  The
+//     chosen columns, ascending, are then copied to the output row, padded
+//     with -1 to k.
+constexpr int kShortWaves = 4;  // waves (rows in flight) per workgroup
+
+// Orders this wave's earlier LDS accesses before its later ones, across lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// OR over the 64 lanes (row shifts and broadcasts as in wave_incl_scan).
+__device__ __forceinline__ uint32_t wave_or(uint32_t x) {
+  x |= dpp_or0<0x111, 0xF>(x);
+  x |= dpp_or0<0x112, 0xF>(x);
+  x |= dpp_or0<0x114, 0xF>(x);
+  x |= dpp_or0<0x118, 0xF>(x);
+  x |= dpp_or0<0x142, 0xA>(x);
+  x |= dpp_or0<0x143, 0xC>(x);
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
+
+// Exclusive prefix over the lanes of a packed count, and the wave's total.
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t x, uint32_t* total) {
+  const uint32_t incl = wave_incl_scan(x);
+  *total = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+  return incl - x;
+}
+
+// Writes the 4-key steps v0 .. v0+2 (those below kSteps) of this lane in
+// column order: key j is "taken" when take(j); taken keys land at
+// dst[base + (taken keys before them)] and the others at dst[spare];
+// base advances by the step group's total.  One wave scan of three 10-bit
+// counts (at most 4 per lane and step, 256 per wave) serves the group.
+template <int kSteps, typename Take, typename Val, typename Dst>
+__device__ __forceinline__ void place_group(int v0, uint32_t& base, uint32_t spare, Take take,
+                                            Val val, Dst* dst) {
+  uint32_t packed = 0u;
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    if (v0 + s < kSteps) {
+      uint32_t c = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c += take(4 * (v0 + s) + i);
+      packed |= c << (10 * s);
+    }
+  }
+  uint32_t tot;
+  const uint32_t ex = wave_excl_scan(packed, &tot);
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    if (v0 + s < kSteps) {
+      uint32_t pos = base + ((ex >> (10 * s)) & 1023u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 4 * (v0 + s) + i;
+        const bool t = take(j);
+        dst[t ? pos : spare] = val(j);
+        pos += t;
+      }
+      base += (tot >> (10 * s)) & 1023u;
+    }
+  }
+}
+
+template <int KPL>
+__global__ void __launch_bounds__(64 * kShortWaves)
+topk_short_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride,
+                  int64_t q_pos0, int topk, int cap, int wave_words,
+                  int32_t* __restrict__ out_idx) {
+  static_assert(KPL % 4 == 0 && KPL <= 64, "keys per lane");
+  constexpr int kSteps = KPL / 4;
+  // per wave: the histogram (kBins words) while the threshold is found, then
+  // the chosen columns (cap of them, each < 4,096) + one spare slot per lane
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds_all[];
+  __shared__ uint32_t cand_all[kShortWaves][128];  // bin list, then one spare slot per lane
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kShortWaves + wave;
+  if (row >= rows) return;
+  uint32_t* const hist = lds_all + wave * wave_words;
+  uint16_t* const ob = reinterpret_cast<uint16_t*>(hist);
+  uint32_t* const cand = cand_all[wave];
+  const int vis = static_cast<int>(visible_rows(q_pos0 + row));
+  const int need = vis < topk ? vis : topk;  // <= cap
+  int32_t* const dst = out_idx + row * static_cast<int64_t>(topk);
+
+  if (need < vis) {
+    const float* src = scores + row * stride;
+    // loads: lanes past the prefix re-read its last float4 (rows hold
+    // `stride` >= vis floats with stride % 4 == 0, so that float4 is in
+    // bounds); their keys are cleared below
+    const int clast = (vis - 1) & ~3;
+    float4 x[kSteps];
+#pragma unroll
+    for (int v = 0; v < kSteps; ++v) {
+      const int c = 256 * v + 4 * lane;
+      x[v] = *reinterpret_cast<const float4*>(src + (c < clast ? c : clast));
+    }
+    uint32_t key[KPL];
+    uint32_t kor = 0u, nor = 0u;  // OR of the valid keys, and of their complements
+#pragma unroll
+    for (int v = 0; v < kSteps; ++v) {
+      uint32_t k0 = float_key(x[v].x), k1 = float_key(x[v].y);
+      uint32_t k2 = float_key(x[v].z), k3 = float_key(x[v].w);
+      if (256 * v + 256 > vis) {  // uniform: this step reaches past the prefix
+        const int c = 256 * v + 4 * lane;
+        k0 = c < vis ? k0 : 0u;
+        k1 = c + 1 < vis ? k1 : 0u;
+        k2 = c + 2 < vis ? k2 : 0u;
+        k3 = c + 3 < vis ? k3 : 0u;
+        nor |= (k0 ? ~k0 : 0u) | (k1 ? ~k1 : 0u) | (k2 ? ~k2 : 0u) | (k3 ? ~k3 : 0u);
+      } else {
+        nor |= ~k0 | ~k1 | ~k2 | ~k3;
+      }
+      kor |= k0 | k1 | k2 | k3;
+      key[4 * v] = k0;
+      key[4 * v + 1] = k1;
+      key[4 * v + 2] = k2;
+      key[4 * v + 3] = k3;
+    }
+    kor = wave_or(kor);
+    nor = wave_or(nor);
+    const uint32_t diff = kor & nor;  // bits in which the valid keys differ
+    uint32_t remaining = static_cast<uint32_t>(need);
+    uint32_t prefix, mask, n_eq;
+    int shift;
+    if (diff == 0u) {  // one value
+      prefix = kor;
+      mask = 0xffffffffu;
+      shift = 0;
+      n_eq = static_cast<uint32_t>(vis);
+    } else {
+      const int hb = 31 - __builtin_clz(diff);
+      mask = (hb == 31) ? 0u : ~((2u << hb) - 1u);
+      prefix = kor & mask;
+      shift = hb + 1;
+      n_eq = 0u;
+    }
+    bool first_pass = true;
+    while (shift > 0) {
+      // the keys pass through an empty asm, so that per-key tests are made in
+      // each pass rather than hoisted out of this loop as 64 lane masks
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) asm volatile("" : "+v"(key[j]));
+      const int dbits = shift < 11 ? shift : 11;
+      shift -= dbits;
+      const uint32_t dmask = (1u << dbits) - 1u;
+#pragma unroll
+      for (int v = 0; v < 8; ++v)
+        *reinterpret_cast<u32x4_t*>(&hist[32 * lane + 4 * v]) = u32x4_t{0u, 0u, 0u, 0u};
+      wave_lds_sync();
+#pragma unroll
+      for (int v = 0; v < kSteps; ++v) {
+        // the first pass counts every valid key (all share the prefix)
+        if (first_pass && 256 * v + 256 <= vis) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) atomicAdd(&hist[(key[4 * v + i] >> shift) & dmask], 1u);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t k = key[4 * v + i];
+            if (k && (k & mask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
+          }
+        }
+      }
+      first_pass = false;
+      wave_lds_sync();
+      // lane l owns bins 32l .. 32l + 31 as 8 groups of 4; keys in higher
+      // lanes' bins are larger.  The lane holding the k-th key is found by a
+      // wave scan, then (in every lane, for its own bins) the group and bin.
+      uint32_t gs[8];
+      uint32_t own = 0u;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const u32x4_t q4 = *reinterpret_cast<const u32x4_t*>(&hist[32 * lane + 4 * v]);
+        gs[v] = q4[0] + q4[1] + q4[2] + q4[3];
+        own += gs[v];
+      }
+      const uint32_t pre = wave_incl_scan(own);
+      const uint32_t all =
+          static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(pre), 63));
+      const uint32_t above = all - pre;
+      uint32_t cum = above;
+      int gv = 0;
+      bool found = false;
+#pragma unroll
+      for (int v = 7; v >= 0; --v) {
+        const bool f = !found && cum + gs[v] >= remaining;
+        gv = f ? v : gv;
+        cum += (found || f) ? 0u : gs[v];
+        found = found || f;
+      }
+      const u32x4_t q4 = *reinterpret_cast<const u32x4_t*>(&hist[32 * lane + 4 * gv]);
+      uint32_t b = 0u, cnt = q4[0];
+      found = false;
+#pragma unroll
+      for (int i = 3; i >= 1; --i) {
+        const bool f = !found && cum + q4[i] >= remaining;
+        b = f ? static_cast<uint32_t>(i) : b;
+        cnt = f ? q4[i] : cnt;
+        cum += (found || f) ? 0u : q4[i];
+        found = found || f;
+      }
+      // exactly one lane holds the bin: above < remaining <= above + own
+      const uint64_t hit = __ballot(above < remaining && remaining <= above + own);
+      const int hl = hit ? __builtin_ctzll(hit) : 0;
+      const uint32_t bin = static_cast<uint32_t>(
+          __builtin_amdgcn_readlane(static_cast<int>(32 * lane + 4 * gv + b), hl));
+      remaining -= static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(cum), hl));
+      const uint32_t in_bin =
+          static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(cnt), hl));
+      prefix |= bin << shift;
+      mask |= dmask << shift;
+      n_eq = in_bin;  // the count of keys equal to T once shift reaches 0
+      wave_lds_sync();  // the histogram is read before it is cleared or reused
+      if (shift > 0 && in_bin <= 64u) {
+        // list the bin's keys, one per lane: exactly in_bin keys match (the
+        // bin's count), so the list positions stay below 64
+        uint32_t base = 0u;
+#pragma unroll
+        for (int v0 = 0; v0 < kSteps; v0 += 3) {
+          if (base >= in_bin) continue;  // uniform: the list is complete
+          place_group<kSteps>(
+              v0, base, 64u + lane,
+              [&](int j) {
+                const uint32_t k = key[j];
+                // only steps reaching past the prefix hold key 0 (uniform test)
+                return (256 * (j >> 2) + 256 <= vis || k != 0u) && (k & mask) == prefix;
+              },
+              [&](int j) { return key[j]; }, cand);
+        }
+        wave_lds_sync();
+        const bool in_list = static_cast<uint32_t>(lane) < in_bin;
+        const uint32_t xk = in_list ? cand[lane] : 0u;
+        bool alive = in_list;
+        for (int bb = shift - 1; bb >= 0; --bb) {
+          const bool one = alive && ((xk >> bb) & 1u);
+          const uint32_t c1 = static_cast<uint32_t>(__popcll(__ballot(one)));
+          if (c1 >= remaining) {
+            prefix |= 1u << bb;
+            alive = one;
+          } else {
+            remaining -= c1;
+            alive = alive && !one;
+          }
+        }
+        n_eq = static_cast<uint32_t>(__popcll(__ballot(alive)));
+        shift = 0;
+        wave_lds_sync();  // the list is read before any later write
+      }
+    }
+    const uint32_t T = prefix, need_eq = remaining;
+
+    // ---- ordered emission into the wave's LDS row (over the histogram)
+    uint32_t base = 0u;
+    const uint32_t spare = static_cast<uint32_t>(cap + lane);
+    auto col = [&](int j) { return static_cast<uint16_t>(256 * (j >> 2) + 4 * lane + (j & 3)); };
+    if (n_eq == need_eq) {
+      // every key equal to T is chosen: the choice is key >= T (T > 0, so
+      // cleared keys are never chosen); exactly `need` keys qualify
+#pragma unroll
+      for (int v0 = 0; v0 < kSteps; v0 += 3) {
+        if (base >= static_cast<uint32_t>(need)) continue;  // uniform: all placed
+        place_group<kSteps>(v0, base, spare, [&](int j) { return key[j] >= T; }, col, ob);
+      }
+    } else {
+      // some keys equal to T are left out: keys > T, and the first need_eq
+      // keys == T in column order
+      uint32_t eq_base = 0u;
+      const uint32_t n_gt = static_cast<uint32_t>(need) - need_eq;
+#pragma unroll
+      for (int v = 0; v < kSteps; ++v) {
+        if (base >= n_gt && eq_base >= need_eq) continue;  // uniform: all placed
+        uint32_t c = 0u;  // (keys > T) | (keys == T) << 16 of this lane's step
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          c += static_cast<uint32_t>(key[4 * v + i] > T) |
+               (static_cast<uint32_t>(key[4 * v + i] == T) << 16);
+        uint32_t tot;
+        const uint32_t ex = wave_excl_scan(c, &tot);
+        uint32_t g = base + (ex & 0xffffu), e = eq_base + (ex >> 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t k = key[4 * v + i];
+          const bool gt = k > T, eq = k == T;
+          const bool ch = gt || (eq && e < need_eq);
+          ob[ch ? g + (e < need_eq ? e : need_eq) : spare] = col(4 * v + i);
+          g += gt;
+          e += eq;
+        }
+        base += tot & 0xffffu;
+        eq_base += tot >> 16;
+      }
+    }
+    wave_lds_sync();
+    if ((topk & 3) == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+      for (int j = 4 * lane; j < topk; j += 256) {
+        uint2 w = make_uint2(0u, 0u);
+        if (j < need) w = *reinterpret_cast<const uint2*>(&ob[j]);  // inside the row's slots
+        int4 o;
+        o.x = j < need ? static_cast<int>(w.x & 0xffffu) : -1;
+        o.y = j + 1 < need ? static_cast<int>(w.x >> 16) : -1;
+        o.z = j + 2 < need ? static_cast<int>(w.y & 0xffffu) : -1;
+        o.w = j + 3 < need ? static_cast<int>(w.y >> 16) : -1;
+        *reinterpret_cast<int4*>(dst + j) = o;
+      }
+    } else {
+      for (int j = lane; j < topk; j += 64) {
+        int o = -1;
+        if (j < need) o = ob[j];
+        dst[j] = o;
+      }
+    }
+  } else {
+    // every visible column is chosen
+    for (int j = lane; j < topk; j += 64) dst[j] = j < need ? j : -1;
+  }
+}
+
+// Longest row the short-row kernel takes.
+constexpr int64_t kShortMaxVis = 64 * 64;
+
+hipError_t launch_short(const float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
+                        int32_t topk, int32_t* out_idx, hipStream_t s) {
+  const int64_t max_vis = (q_pos0 + rows) / 4;
+  const dim3 grid(static_cast<unsigned>((rows + kShortWaves - 1) / kShortWaves));
+  const dim3 block(64 * kShortWaves);
+  // LDS of each wave: the histogram, later min(k, longest row) chosen
+  // columns (16-bit) + 64 spare slots; a multiple of 4 words
+  const int cap = static_cast<int>(max_vis < topk ? max_vis : topk);
+  int words = (cap + 64 + 1) / 2;
+  if (words < kBins) words = kBins;
+  words = (words + 3) & ~3;
+  const size_t lds = static_cast<size_t>(kShortWaves) * words * sizeof(uint32_t);
+  if (max_vis <= 1024)
+    hipLaunchKernelGGL(topk_short_kernel<16>, grid, block, lds, s, scores, rows, stride, q_pos0,
+                       topk, cap, words, out_idx);
+  else if (max_vis <= 2048)
+    hipLaunchKernelGGL(topk_short_kernel<32>, grid, block, lds, s, scores, rows, stride, q_pos0,
+                       topk, cap, words, out_idx);
+  else
+    hipLaunchKernelGGL(topk_short_kernel<64>, grid, block, lds, s, scores, rows, stride, q_pos0,
+                       topk, cap, words, out_idx);
+  return hipGetLastError();
+}
+
 template <int CPT, int PER>
 hipError_t launch_cpt(const float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
                       int32_t topk, int32_t* out_idx, int64_t fixed_n, const int32_t* remap,
@@ -683,6 +1048,9 @@ hipError_t launch_rows(const float* scores, int64_t rows, int64_t stride, int64_
 hipError_t dsv4_launch_topk(const float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
                             int32_t topk, int32_t* out_idx, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  const bool aligned = (stride & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
+  if (aligned && (q_pos0 + rows) / 4 <= kShortMaxVis)
+    return launch_short(scores, rows, stride, q_pos0, topk, out_idx, s);
   return launch_rows(scores, rows, stride, q_pos0, topk, out_idx, -1, nullptr, s);
 }
 

@@ -1,0 +1,116 @@
+"""Top-k of short rows (at most 4,096 visible columns), where one wave holds a
+whole row: parity with the oracle's selection and with the workgroup-per-row
+kernel, which the same entry point takes when the row stride is not a
+multiple of 4 floats.
+
+Sizes put the longest row exactly at, and one past, each register layout's
+limit (1,024 / 2,048 / 4,096 columns; 4,097 goes to the workgroup kernel).
+Row contents cover the selection's hard cases: several digit passes (few
+distinct values), a single value, signed zeros, keys spanning the sign bit
+and infinities, and k at or above the visible count.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_indexed_attention_amd as dsv4
+from oracle import dsv4_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(kind, rows, n_cols, rng):
+    shape = (rows, n_cols)
+    if kind == "relu_sum":      # indexer-like: non-negative, tightly packed exponents
+        s = np.maximum(rng.standard_normal((rows, n_cols, 8)), 0).sum(-1)
+    elif kind == "uniform":
+        s = rng.random(shape)
+    elif kind == "normal":
+        s = rng.standard_normal(shape)
+    elif kind == "levels3":
+        s = rng.integers(0, 3, size=shape)
+    elif kind == "levels40":
+        s = rng.integers(0, 40, size=shape) * 0.25
+    elif kind == "constant":
+        s = np.full(shape, 0.75)
+    elif kind == "signed_zero":
+        s = np.where(rng.random(shape) < 0.5, -0.0, 0.0)
+        s[:, ::37] = 2.0
+    elif kind == "wide":        # mixed signs, huge range, infinities
+        s = rng.standard_normal(shape) * np.exp2(rng.integers(-90, 90, size=shape))
+        s[:, ::53] = np.inf
+        s[:, 7::61] = -np.inf
+    else:
+        raise ValueError(kind)
+    return s.astype(np.float32)
+
+
+def _select(scores, q_pos0, n_cols, topk, stride):
+    rows = scores.shape[0]
+    buf = np.full((rows, stride), np.float32(3e38), np.float32)  # garbage past the prefix
+    buf[:, :n_cols] = scores
+    for t in range(rows):
+        buf[t, O.visible_rows(q_pos0 + t):n_cols] = np.float32(3e38)
+    d = torch.from_numpy(buf).cuda()
+    out = torch.full((rows, topk), 77, dtype=torch.int32, device="cuda")
+    dsv4.dsv4_topk_select(d, q_pos0, n_cols, topk, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), buf
+
+
+@pytest.mark.parametrize("max_vis", [1024, 1025, 2048, 2049, 4096, 4097])
+@pytest.mark.parametrize("kind", ["relu_sum", "uniform", "normal", "levels3", "levels40",
+                                  "constant", "signed_zero", "wide"])
+def test_short_rows_match_oracle(max_vis, kind):
+    rng = np.random.default_rng(zlib.crc32(f"{kind}/{max_vis}".encode()))
+    rows = 70                                 # 18 workgroups of 4 waves, the last one partial
+    q_pos0 = 4 * max_vis - rows               # the last row sees exactly max_vis columns
+    n_cols = max_vis
+    topk = 512 if max_vis <= 2049 else 2048
+    s = _rows(kind, rows, n_cols, rng)
+    got, buf = _select(s, q_pos0, n_cols, topk, stride=n_cols + (-n_cols) % 4)
+    want = O.topk_select(buf.astype(np.float64), q_pos0, topk)
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("topk", [1, 2, 63, 64, 65, 1000, 1023, 1024, 4096])
+def test_short_rows_k_around_visible(topk):
+    """k below, at and above the visible count of every row (rows see 768..1,023
+    columns here; k >= visible chooses every visible column)."""
+    rng = np.random.default_rng(topk)
+    rows, q_pos0 = 1024, 3072 - 1
+    n_cols = (q_pos0 + rows) // 4
+    s = _rows("relu_sum", rows, n_cols, rng)
+    got, buf = _select(s, q_pos0, n_cols, topk, stride=n_cols + (-n_cols) % 4)
+    np.testing.assert_array_equal(got, O.topk_select(buf.astype(np.float64), q_pos0, topk))
+
+
+def test_short_rows_from_the_first_token():
+    """Rows 0-2 see no pooled row (all -1); row 3 sees one."""
+    rng = np.random.default_rng(5)
+    rows, q_pos0, topk = 200, 0, 16
+    n_cols = 52
+    s = _rows("normal", rows, n_cols, rng)
+    got, buf = _select(s, q_pos0, n_cols, topk, stride=52)
+    assert (got[:3] == -1).all() and got[3, 0] == 0 and (got[3, 1:] == -1).all()
+    np.testing.assert_array_equal(got, O.topk_select(buf.astype(np.float64), q_pos0, topk))
+
+
+@pytest.mark.parametrize("kind", ["relu_sum", "levels3", "wide"])
+def test_short_rows_match_workgroup_kernel(kind):
+    """A whole 2,048-row tile at a 16K-token context (4,096 pooled rows, k =
+    2,048): the wave-per-row kernel (row stride 4,096) against the
+    workgroup-per-row kernel (row stride 4,097, not a multiple of 4)."""
+    rng = np.random.default_rng(zlib.crc32(kind.encode()))
+    rows, q_pos0, topk = 2048, 16384 - 2048, 2048
+    n_cols = (q_pos0 + rows) // 4
+    s = _rows(kind, rows, n_cols, rng)
+    a, _ = _select(s, q_pos0, n_cols, topk, stride=n_cols)
+    b, _ = _select(s, q_pos0, n_cols, topk, stride=n_cols + 1)
+    np.testing.assert_array_equal(a, b)
+    pick = rng.choice(rows, 64, replace=False)
+    for t in pick:
+        vis = O.visible_rows(q_pos0 + int(t))
+        np.testing.assert_array_equal(a[t], O.topk_row(s[t].astype(np.float64), vis, topk))
