@@ -722,39 +722,64 @@ __device__ __forceinline__ void place_group(int v0, uint32_t& base, uint32_t spa
   }
 }
 
-template <int KPL>
-__global__ void __launch_bounds__(64 * kShortWaves)
-topk_short_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride,
-                  int64_t q_pos0, int topk, int cap, int wave_words,
-                  int32_t* __restrict__ out_idx) {
+template <int KPL, int NW>
+__global__ void __launch_bounds__(64 * (NW == 1 ? kShortWaves : NW), 4)
+topk_reg_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int64_t q_pos0,
+                int topk, int cap, int words, int32_t* __restrict__ out_idx) {
   static_assert(KPL % 4 == 0 && KPL <= 64, "keys per lane");
+  static_assert(NW == 1 || KPL == 64, "rows of several waves hold 4,096 columns per wave");
   constexpr int kSteps = KPL / 4;
-  // per wave: the histogram (kBins words) while the threshold is found, then
-  // the chosen columns (cap of them, each < 4,096) + one spare slot per lane
+  constexpr int kRowsPerWG = NW == 1 ? kShortWaves : 1;
+  constexpr int kCols = 64 * KPL;  // columns of one wave
+  // per row: the histogram (two of kBins words when several waves share the
+  // row, so that one can be cleared while the other is read) while the
+  // threshold is found, then the chosen columns (cap of them, 16-bit) + one
+  // spare slot per lane
   extern __shared__ __attribute__((aligned(16))) uint32_t lds_all[];
-  __shared__ uint32_t cand_all[kShortWaves][128];  // bin list, then one spare slot per lane
+  __shared__ uint32_t cand_all[kRowsPerWG * NW][128];  // per wave: bin list + spare slots
+  __shared__ uint32_t xch[4][NW];                       // cross-wave exchange (NW > 1)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kShortWaves + wave;
-  if (row >= rows) return;
-  uint32_t* const hist = lds_all + wave * wave_words;
-  uint16_t* const ob = reinterpret_cast<uint16_t*>(hist);
+  const int rslot = NW == 1 ? wave : 0;  // row of this wave within the workgroup
+  const int wr = NW == 1 ? 0 : wave;     // part of the row held by this wave
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerWG + rslot;
+  if (row >= rows) return;  // NW > 1: the whole workgroup (one row)
+  uint32_t* const row_lds = lds_all + rslot * words;
+  uint16_t* const ob = reinterpret_cast<uint16_t*>(row_lds);
   uint32_t* const cand = cand_all[wave];
   const int vis = static_cast<int>(visible_rows(q_pos0 + row));
   const int need = vis < topk ? vis : topk;  // <= cap
+  const int col0 = wr * kCols;
+  const int nthr = 64 * NW, tid_r = 64 * wr + lane;  // threads of the row, and this one
   int32_t* const dst = out_idx + row * static_cast<int64_t>(topk);
+  auto row_sync = [&]() {
+    if (NW == 1) wave_lds_sync();
+    else __syncthreads();
+  };
+  auto clear_hist = [&](uint32_t* h) {  // the row's threads clear kBins words
+#pragma unroll
+    for (int v = 0; v < kBins / (256 * NW); ++v)
+      *reinterpret_cast<u32x4_t*>(&h[4 * (tid_r + nthr * v)]) = u32x4_t{0u, 0u, 0u, 0u};
+  };
+  auto hist_of = [&](int pass) { return row_lds + (NW > 1 ? (pass & 1) * kBins : 0); };
 
   if (need < vis) {
     const float* src = scores + row * stride;
     // loads: lanes past the prefix re-read its last float4 (rows hold
     // `stride` >= vis floats with stride % 4 == 0, so that float4 is in
-    // bounds); their keys are cleared below
+    // bounds); their keys are cleared below.  A wave wholly past the prefix
+    // loads nothing.
     const int clast = (vis - 1) & ~3;
     float4 x[kSteps];
+    if (col0 < vis) {
 #pragma unroll
-    for (int v = 0; v < kSteps; ++v) {
-      const int c = 256 * v + 4 * lane;
-      x[v] = *reinterpret_cast<const float4*>(src + (c < clast ? c : clast));
+      for (int v = 0; v < kSteps; ++v) {
+        const int c = col0 + 256 * v + 4 * lane;
+        x[v] = *reinterpret_cast<const float4*>(src + (c < clast ? c : clast));
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < kSteps; ++v) x[v] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     uint32_t key[KPL];
     uint32_t kor = 0u, nor = 0u;  // OR of the valid keys, and of their complements
@@ -762,8 +787,8 @@ topk_short_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride
     for (int v = 0; v < kSteps; ++v) {
       uint32_t k0 = float_key(x[v].x), k1 = float_key(x[v].y);
       uint32_t k2 = float_key(x[v].z), k3 = float_key(x[v].w);
-      if (256 * v + 256 > vis) {  // uniform: this step reaches past the prefix
-        const int c = 256 * v + 4 * lane;
+      if (col0 + 256 * v + 256 > vis) {  // uniform: this step reaches past the prefix
+        const int c = col0 + 256 * v + 4 * lane;
         k0 = c < vis ? k0 : 0u;
         k1 = c + 1 < vis ? k1 : 0u;
         k2 = c + 2 < vis ? k2 : 0u;
@@ -780,6 +805,13 @@ topk_short_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride
     }
     kor = wave_or(kor);
     nor = wave_or(nor);
+    if (NW > 1) {
+      if (lane == 0) { xch[0][wr] = kor; xch[1][wr] = nor; }
+      clear_hist(hist_of(0));
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < NW; ++w) { kor |= xch[0][w]; nor |= xch[1][w]; }
+    }
     const uint32_t diff = kor & nor;  // bits in which the valid keys differ
     uint32_t remaining = static_cast<uint32_t>(need);
     uint32_t prefix, mask, n_eq;
@@ -796,7 +828,9 @@ topk_short_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride
       shift = hb + 1;
       n_eq = 0u;
     }
-    bool first_pass = true;
+    // Every decision below depends only on values the row's waves share, so
+    // all of them take the same branches and reach the same barriers.
+    int pass = 0;
     while (shift > 0) {
       // the keys pass through an empty asm, so that per-key tests are made in
       // each pass rather than hoisted out of this loop as 64 lane masks
@@ -805,14 +839,17 @@ topk_short_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride
       const int dbits = shift < 11 ? shift : 11;
       shift -= dbits;
       const uint32_t dmask = (1u << dbits) - 1u;
-#pragma unroll
-      for (int v = 0; v < 8; ++v)
-        *reinterpret_cast<u32x4_t*>(&hist[32 * lane + 4 * v]) = u32x4_t{0u, 0u, 0u, 0u};
-      wave_lds_sync();
+      uint32_t* const hist = hist_of(pass);
+      if (NW == 1) {
+        clear_hist(hist);
+        wave_lds_sync();
+      } else if (pass > 0) {
+        __syncthreads();  // this pass's table was cleared during the previous pass
+      }
 #pragma unroll
       for (int v = 0; v < kSteps; ++v) {
         // the first pass counts every valid key (all share the prefix)
-        if (first_pass && 256 * v + 256 <= vis) {
+        if (pass == 0 && col0 + 256 * v + 256 <= vis) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) atomicAdd(&hist[(key[4 * v + i] >> shift) & dmask], 1u);
         } else {
@@ -823,11 +860,13 @@ topk_short_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride
           }
         }
       }
-      first_pass = false;
-      wave_lds_sync();
+      row_sync();  // every count is in
+      // the other table is no longer read by anyone: clear it for the next pass
+      if (NW > 1) clear_hist(hist_of(pass + 1));
       // lane l owns bins 32l .. 32l + 31 as 8 groups of 4; keys in higher
       // lanes' bins are larger.  The lane holding the k-th key is found by a
       // wave scan, then (in every lane, for its own bins) the group and bin.
+      // Every wave of the row does this on the same table.
       uint32_t gs[8];
       uint32_t own = 0u;
 #pragma unroll
@@ -872,10 +911,10 @@ topk_short_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride
       prefix |= bin << shift;
       mask |= dmask << shift;
       n_eq = in_bin;  // the count of keys equal to T once shift reaches 0
-      wave_lds_sync();  // the histogram is read before it is cleared or reused
+      if (NW == 1) wave_lds_sync();  // the table is read before it is cleared again
       if (shift > 0 && in_bin <= 64u) {
-        // list the bin's keys, one per lane: exactly in_bin keys match (the
-        // bin's count), so the list positions stay below 64
+        // list the bin's keys: exactly in_bin keys match (the bin's count),
+        // so every wave's list stays below 64 entries
         uint32_t base = 0u;
 #pragma unroll
         for (int v0 = 0; v0 < kSteps; v0 += 3) {
@@ -885,13 +924,34 @@ topk_short_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride
               [&](int j) {
                 const uint32_t k = key[j];
                 // only steps reaching past the prefix hold key 0 (uniform test)
-                return (256 * (j >> 2) + 256 <= vis || k != 0u) && (k & mask) == prefix;
+                return (col0 + 256 * (j >> 2) + 256 <= vis || k != 0u) && (k & mask) == prefix;
               },
               [&](int j) { return key[j]; }, cand);
         }
-        wave_lds_sync();
-        const bool in_list = static_cast<uint32_t>(lane) < in_bin;
-        const uint32_t xk = in_list ? cand[lane] : 0u;
+        if (NW > 1 && lane == 0) xch[2][wr] = base;
+        row_sync();
+        // one list entry per lane: the waves' lists in order
+        bool in_list;
+        uint32_t xk = 0u;
+        if (NW == 1) {
+          in_list = static_cast<uint32_t>(lane) < in_bin;
+          if (in_list) xk = cand[lane];
+        } else {
+          uint32_t lo = 0u;
+          int sw = -1;
+          uint32_t si = 0u;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            const uint32_t c = xch[2][w];
+            if (static_cast<uint32_t>(lane) >= lo && static_cast<uint32_t>(lane) < lo + c) {
+              sw = w;
+              si = static_cast<uint32_t>(lane) - lo;
+            }
+            lo += c;
+          }
+          in_list = sw >= 0;
+          if (in_list) xk = cand_all[sw][si];
+        }
         bool alive = in_list;
         for (int bb = shift - 1; bb >= 0; --bb) {
           const bool one = alive && ((xk >> bb) & 1u);
@@ -906,18 +966,44 @@ topk_short_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride
         }
         n_eq = static_cast<uint32_t>(__popcll(__ballot(alive)));
         shift = 0;
-        wave_lds_sync();  // the list is read before any later write
       }
+      ++pass;
     }
     const uint32_t T = prefix, need_eq = remaining;
 
-    // ---- ordered emission into the wave's LDS row (over the histogram)
-    uint32_t base = 0u;
-    const uint32_t spare = static_cast<uint32_t>(cap + lane);
-    auto col = [&](int j) { return static_cast<uint16_t>(256 * (j >> 2) + 4 * lane + (j & 3)); };
-    if (n_eq == need_eq) {
-      // every key equal to T is chosen: the choice is key >= T (T > 0, so
-      // cleared keys are never chosen); exactly `need` keys qualify
+    // ---- ordered emission into the row's LDS slots (over the histogram)
+    const bool all_eq = n_eq == need_eq;  // every key equal to T is chosen
+    uint32_t base = 0u, eq_base = 0u;     // chosen (> T, == T) in earlier columns
+    if (NW > 1) {
+      // this wave's counts; earlier waves' totals give its starting point
+      // (keys >= T) | (keys > T) << 16, one count for both emission paths (a
+      // count per path keeps far more registers live)
+      uint32_t c = 0u;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j)
+        c += static_cast<uint32_t>(key[j] >= T) | (static_cast<uint32_t>(key[j] > T) << 16);
+      uint32_t tot;
+      wave_excl_scan(c, &tot);
+      // recompute the tests below rather than keep 64 lane masks
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) asm volatile("" : "+v"(key[j]));
+      if (lane == 0) xch[3][wr] = tot;
+      __syncthreads();  // also: every wave is done with the histogram
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const uint32_t t = w < wr ? xch[3][w] : 0u;
+        const uint32_t ge = t & 0xffffu, gt = t >> 16;
+        if (all_eq) base += ge;
+        else { base += gt; eq_base += ge - gt; }
+      }
+    }
+    const uint32_t spare = static_cast<uint32_t>(cap + 64 * wr + lane);
+    auto col = [&](int j) {
+      return static_cast<uint16_t>(col0 + 256 * (j >> 2) + 4 * lane + (j & 3));
+    };
+    if (all_eq) {
+      // the choice is key >= T (T > 0, so cleared keys are never chosen);
+      // exactly `need` keys qualify
 #pragma unroll
       for (int v0 = 0; v0 < kSteps; v0 += 3) {
         if (base >= static_cast<uint32_t>(need)) continue;  // uniform: all placed
@@ -926,7 +1012,6 @@ topk_short_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride
     } else {
       // some keys equal to T are left out: keys > T, and the first need_eq
       // keys == T in column order
-      uint32_t eq_base = 0u;
       const uint32_t n_gt = static_cast<uint32_t>(need) - need_eq;
 #pragma unroll
       for (int v = 0; v < kSteps; ++v) {
@@ -952,9 +1037,9 @@ topk_short_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride
         eq_base += tot >> 16;
       }
     }
-    wave_lds_sync();
+    row_sync();
     if ((topk & 3) == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-      for (int j = 4 * lane; j < topk; j += 256) {
+      for (int j = 4 * tid_r; j < topk; j += 4 * nthr) {
         uint2 w = make_uint2(0u, 0u);
         if (j < need) w = *reinterpret_cast<const uint2*>(&ob[j]);  // inside the row's slots
         int4 o;
@@ -965,7 +1050,7 @@ topk_short_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride
         *reinterpret_cast<int4*>(dst + j) = o;
       }
     } else {
-      for (int j = lane; j < topk; j += 64) {
+      for (int j = tid_r; j < topk; j += nthr) {
         int o = -1;
         if (j < need) o = ob[j];
         dst[j] = o;
@@ -973,34 +1058,52 @@ topk_short_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride
     }
   } else {
     // every visible column is chosen
-    for (int j = lane; j < topk; j += 64) dst[j] = j < need ? j : -1;
+    for (int j = tid_r; j < topk; j += nthr) dst[j] = j < need ? j : -1;
   }
 }
 
-// Longest row the short-row kernel takes.
-constexpr int64_t kShortMaxVis = 64 * 64;
+// Longest row the register-resident kernels take (8 waves of 4,096 columns).
+constexpr int64_t kRegMaxVis = 8 * 64 * 64;
 
-hipError_t launch_short(const float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
-                        int32_t topk, int32_t* out_idx, hipStream_t s) {
+hipError_t launch_reg(const float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
+                      int32_t topk, int32_t* out_idx, hipStream_t s) {
   const int64_t max_vis = (q_pos0 + rows) / 4;
-  const dim3 grid(static_cast<unsigned>((rows + kShortWaves - 1) / kShortWaves));
-  const dim3 block(64 * kShortWaves);
-  // LDS of each wave: the histogram, later min(k, longest row) chosen
-  // columns (16-bit) + 64 spare slots; a multiple of 4 words
-  const int cap = static_cast<int>(max_vis < topk ? max_vis : topk);
-  int words = (cap + 64 + 1) / 2;
-  if (words < kBins) words = kBins;
-  words = (words + 3) & ~3;
-  const size_t lds = static_cast<size_t>(kShortWaves) * words * sizeof(uint32_t);
-  if (max_vis <= 1024)
-    hipLaunchKernelGGL(topk_short_kernel<16>, grid, block, lds, s, scores, rows, stride, q_pos0,
-                       topk, cap, words, out_idx);
-  else if (max_vis <= 2048)
-    hipLaunchKernelGGL(topk_short_kernel<32>, grid, block, lds, s, scores, rows, stride, q_pos0,
-                       topk, cap, words, out_idx);
+  const int cap = static_cast<int>(max_vis < topk ? max_vis : topk);  // chosen slots per row
+  if (max_vis <= 64 * 64) {
+    // one wave per row, kShortWaves rows per workgroup; per wave the
+    // histogram, later the chosen columns + 64 spare slots (16-bit)
+    const dim3 grid(static_cast<unsigned>((rows + kShortWaves - 1) / kShortWaves));
+    const dim3 block(64 * kShortWaves);
+    int words = (cap + 64 + 1) / 2;
+    if (words < kBins) words = kBins;
+    words = (words + 3) & ~3;
+    const size_t lds = static_cast<size_t>(kShortWaves) * words * sizeof(uint32_t);
+    if (max_vis <= 1024)
+      hipLaunchKernelGGL((topk_reg_kernel<16, 1>), grid, block, lds, s, scores, rows, stride,
+                         q_pos0, topk, cap, words, out_idx);
+    else if (max_vis <= 2048)
+      hipLaunchKernelGGL((topk_reg_kernel<32, 1>), grid, block, lds, s, scores, rows, stride,
+                         q_pos0, topk, cap, words, out_idx);
+    else
+      hipLaunchKernelGGL((topk_reg_kernel<64, 1>), grid, block, lds, s, scores, rows, stride,
+                         q_pos0, topk, cap, words, out_idx);
+    return hipGetLastError();
+  }
+  // one row per workgroup of NW waves; two histograms per row, later the
+  // chosen columns + 64 spare slots per wave (cap + 64 NW <= 4,608 16-bit
+  // slots, inside the 2 x kBins words)
+  const int words = 2 * kBins;
+  const size_t lds = static_cast<size_t>(words) * sizeof(uint32_t);
+  const dim3 grid(static_cast<unsigned>(rows));
+  if (max_vis <= 2 * 64 * 64)
+    hipLaunchKernelGGL((topk_reg_kernel<64, 2>), grid, dim3(128), lds, s, scores, rows, stride,
+                       q_pos0, topk, cap, words, out_idx);
+  else if (max_vis <= 4 * 64 * 64)
+    hipLaunchKernelGGL((topk_reg_kernel<64, 4>), grid, dim3(256), lds, s, scores, rows, stride,
+                       q_pos0, topk, cap, words, out_idx);
   else
-    hipLaunchKernelGGL(topk_short_kernel<64>, grid, block, lds, s, scores, rows, stride, q_pos0,
-                       topk, cap, words, out_idx);
+    hipLaunchKernelGGL((topk_reg_kernel<64, 8>), grid, dim3(512), lds, s, scores, rows, stride,
+                       q_pos0, topk, cap, words, out_idx);
   return hipGetLastError();
 }
 
@@ -1049,8 +1152,8 @@ hipError_t dsv4_launch_topk(const float* scores, int64_t rows, int64_t stride, i
                             int32_t topk, int32_t* out_idx, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   const bool aligned = (stride & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
-  if (aligned && (q_pos0 + rows) / 4 <= kShortMaxVis)
-    return launch_short(scores, rows, stride, q_pos0, topk, out_idx, s);
+  if (aligned && (q_pos0 + rows) / 4 <= kRegMaxVis)
+    return launch_reg(scores, rows, stride, q_pos0, topk, out_idx, s);
   return launch_rows(scores, rows, stride, q_pos0, topk, out_idx, -1, nullptr, s);
 }
 

@@ -1,10 +1,12 @@
-"""Top-k of short rows (at most 4,096 visible columns), where one wave holds a
-whole row: parity with the oracle's selection and with the workgroup-per-row
+"""Top-k of rows held in registers (at most 32,768 visible columns: one wave
+per row up to 4,096 columns, else 2, 4 or 8 waves of 4,096 columns each):
+parity with the oracle's selection and with the LDS-staged workgroup
 kernel, which the same entry point takes when the row stride is not a
-multiple of 4 floats.
+multiple of 4 floats or rows are longer.
 
 Sizes put the longest row exactly at, and one past, each register layout's
-limit (1,024 / 2,048 / 4,096 columns; 4,097 goes to the workgroup kernel).
+limit (1,024 / 2,048 / 4,096 columns in one wave, 8,192 / 16,384 / 32,768 in
+2 / 4 / 8 waves; 32,769 goes to the LDS-staged kernel).
 Row contents cover the selection's hard cases: several digit passes (few
 distinct values), a single value, signed zeros, keys spanning the sign bit
 and infinities, and k at or above the visible count.
@@ -24,7 +26,9 @@ pytestmark = pytest.mark.gpu
 def _rows(kind, rows, n_cols, rng):
     shape = (rows, n_cols)
     if kind == "relu_sum":      # indexer-like: non-negative, tightly packed exponents
-        s = np.maximum(rng.standard_normal((rows, n_cols, 8)), 0).sum(-1)
+        s = np.zeros(shape, np.float32)
+        for _ in range(8):
+            s += np.maximum(rng.standard_normal(shape, dtype=np.float32), 0)
     elif kind == "uniform":
         s = rng.random(shape)
     elif kind == "normal":
@@ -39,7 +43,8 @@ def _rows(kind, rows, n_cols, rng):
         s = np.where(rng.random(shape) < 0.5, -0.0, 0.0)
         s[:, ::37] = 2.0
     elif kind == "wide":        # mixed signs, huge range, infinities
-        s = rng.standard_normal(shape) * np.exp2(rng.integers(-90, 90, size=shape))
+        s = rng.standard_normal(shape, dtype=np.float32) * np.exp2(
+            rng.integers(-90, 90, size=shape).astype(np.float32))
         s[:, ::53] = np.inf
         s[:, 7::61] = -np.inf
     else:
@@ -60,12 +65,13 @@ def _select(scores, q_pos0, n_cols, topk, stride):
     return out.cpu().numpy(), buf
 
 
-@pytest.mark.parametrize("max_vis", [1024, 1025, 2048, 2049, 4096, 4097])
+@pytest.mark.parametrize("max_vis", [1024, 1025, 2048, 2049, 4096, 4097, 8192, 8193, 16384,
+                                     16385, 32768, 32769])
 @pytest.mark.parametrize("kind", ["relu_sum", "uniform", "normal", "levels3", "levels40",
                                   "constant", "signed_zero", "wide"])
 def test_short_rows_match_oracle(max_vis, kind):
     rng = np.random.default_rng(zlib.crc32(f"{kind}/{max_vis}".encode()))
-    rows = 70                                 # 18 workgroups of 4 waves, the last one partial
+    rows = 70                                 # one wave per row: 18 workgroups, the last partial
     q_pos0 = 4 * max_vis - rows               # the last row sees exactly max_vis columns
     n_cols = max_vis
     topk = 512 if max_vis <= 2049 else 2048
@@ -112,5 +118,22 @@ def test_short_rows_match_workgroup_kernel(kind):
     np.testing.assert_array_equal(a, b)
     pick = rng.choice(rows, 64, replace=False)
     for t in pick:
+        vis = O.visible_rows(q_pos0 + int(t))
+        np.testing.assert_array_equal(a[t], O.topk_row(s[t].astype(np.float64), vis, topk))
+
+
+@pytest.mark.parametrize("kind", ["relu_sum", "levels40", "wide"])
+def test_long_rows_match_workgroup_kernel(kind):
+    """A whole 2,048-row tile at a 128K-token context (32,768 pooled rows, k =
+    2,048): the 8-wave register kernel (row stride 32,768) against the
+    LDS-staged kernel (row stride 32,769), and sampled rows against the oracle."""
+    rng = np.random.default_rng(zlib.crc32(("long/" + kind).encode()))
+    rows, q_pos0, topk = 2048, 131072 - 2048, 2048
+    n_cols = (q_pos0 + rows) // 4
+    s = _rows(kind, rows, n_cols, rng)
+    a, _ = _select(s, q_pos0, n_cols, topk, stride=n_cols)
+    b, _ = _select(s, q_pos0, n_cols, topk, stride=n_cols + 1)
+    np.testing.assert_array_equal(a, b)
+    for t in rng.choice(rows, 24, replace=False):
         vis = O.visible_rows(q_pos0 + int(t))
         np.testing.assert_array_equal(a[t], O.topk_row(s[t].astype(np.float64), vis, topk))
