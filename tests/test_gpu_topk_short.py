@@ -137,3 +137,35 @@ def test_long_rows_match_workgroup_kernel(kind):
     for t in rng.choice(rows, 24, replace=False):
         vis = O.visible_rows(q_pos0 + int(t))
         np.testing.assert_array_equal(a[t], O.topk_row(s[t].astype(np.float64), vis, topk))
+
+
+@pytest.mark.parametrize("max_vis,topk", [(32768, 4096), (16384, 4096), (4096, 4095),
+                                          (2048, 1023), (32768, 3), (1024, 1)])
+def test_register_rows_large_and_odd_k(max_vis, topk):
+    """The largest k (its output slots fill most of a multi-wave row's LDS
+    area), odd k (the scalar copy-out), and tiny k."""
+    rng = np.random.default_rng(max_vis + topk)
+    rows = 40
+    q_pos0 = 4 * max_vis - rows
+    s = _rows("relu_sum", rows, max_vis, rng)
+    got, buf = _select(s, q_pos0, max_vis, topk, stride=max_vis)
+    np.testing.assert_array_equal(got, O.topk_select(buf.astype(np.float64), q_pos0, topk))
+
+
+@pytest.mark.parametrize("max_vis", [1024, 4096, 32768])
+def test_register_rows_unaligned_output(max_vis):
+    """An output row block that starts 4 bytes past a 16-byte boundary takes
+    the element-wise copy-out."""
+    rng = np.random.default_rng(max_vis)
+    rows, topk = 36, 512
+    q_pos0 = 4 * max_vis - rows
+    s = _rows("normal", rows, max_vis, rng)
+    d = torch.from_numpy(s).cuda()
+    flat = torch.full((rows * topk + 1,), 77, dtype=torch.int32, device="cuda")
+    out = flat[1:].view(rows, topk)
+    assert out.data_ptr() % 16 == 4
+    dsv4.dsv4_topk_select(d, q_pos0, max_vis, topk, out)
+    torch.cuda.synchronize()
+    assert int(flat[0]) == 77                 # nothing written before the block
+    np.testing.assert_array_equal(out.cpu().numpy(),
+                                  O.topk_select(s.astype(np.float64), q_pos0, topk))
