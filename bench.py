@@ -563,8 +563,19 @@ def run_workload(args, wl: SI.Workload, extras: bool) -> dict:
     q_t, w_t = setup.q_idx[t_last0:], setup.w[t_last0:]
     ms_score = timed_kernel(lambda: d.dsv4_indexer_scores(setup.icache, q_t, w_t, wl.q_pos0 + t_last0,
                                                           sc_view, True), max(5, args.steps))
-    ms_topk = timed_kernel(lambda: d.dsv4_topk_select(sc_view, wl.q_pos0 + t_last0, S, wl.topk,
-                                                      setup.idx[t_last0:]), max(5, args.steps))
+    # the top-k the select runs: over rows longer than one 32,768-column chunk,
+    # the two-pass chunk top-k (timed here with a workspace, so that the scores
+    # just written stay intact; the select keeps the chunk winners in its
+    # scratch instead), else the per-row kernel
+    split_ws = d.dsv4_topk_split_workspace_bytes(tile, wl.q_pos0 + t_last0, wl.topk)
+    if split_ws > 0:
+        ws_t = torch.empty(split_ws // 4, dtype=torch.float32, device="cuda")
+        topk_fn = lambda: d.dsv4_topk_select_split(sc_view, wl.q_pos0 + t_last0, S, wl.topk,
+                                                   setup.idx[t_last0:], ws_t)
+    else:
+        topk_fn = lambda: d.dsv4_topk_select(sc_view, wl.q_pos0 + t_last0, S, wl.topk,
+                                             setup.idx[t_last0:])
+    ms_topk = timed_kernel(topk_fn, max(5, args.steps))
     flops_per_pair = 2 * wl.idx_heads * wl.idx_dim
     score_tflops = tile_pairs * flops_per_pair / (ms_score * 1e-3) / 1e12
     topk_bytes = tile_pairs * 4 + tile * wl.topk * 4

@@ -171,15 +171,16 @@ int dsv4_topk_select(const float* scores, int64_t rows, int64_t stride, int64_t 
                      int64_t n_cols, int32_t topk, int32_t* out_idx, void* stream);
 
 /*
- * Chunk-parallel top-k for a few long rows (narrow-query steps: decode,
- * draft verification, short prefill bands at long context [P1 scope; P4]).
- * Same arguments, rule and output as dsv4_topk_select, bit for bit, plus a
- * caller-owned device workspace (16-byte aligned).  When 1 <= rows <= 64,
- * the longest visible prefix spans more than one 32,768-column chunk and
- * the first row sees at least topk columns, every (row, chunk) pair is
- * selected by its own workgroup and a second pass selects each row's top-k
- * among the chunk winners; otherwise it runs dsv4_topk_select's kernel and
- * the workspace is unused (may be NULL).
+ * Chunk-parallel top-k for long rows (narrow-query steps: decode, draft
+ * verification, short prefill bands at long context [P1 scope; P4]; and
+ * whole tiles at 1M context).  Same arguments, rule and output as
+ * dsv4_topk_select, bit for bit, plus a caller-owned device workspace
+ * (16-byte aligned).  When the longest visible prefix spans more than one
+ * 32,768-column chunk, the first row sees at least topk columns, and either
+ * rows <= 64 or (topk % 4 == 0 and chunks * topk <= 32,768), every
+ * (row, chunk) pair is selected by its own workgroup and a second pass
+ * selects each row's top-k among the chunk winners; otherwise it runs
+ * dsv4_topk_select's kernel and the workspace is unused (may be NULL).
  * dsv4_topk_split_workspace_bytes writes the workspace bytes needed (0 when
  * the two-pass path does not apply).
  * Errors: as dsv4_topk_select; INVALID_ARG (workspace NULL / misaligned when
@@ -199,11 +200,15 @@ int dsv4_topk_select_split(const float* scores, int64_t rows, int64_t stride, in
  *   3. If S == 0: every slot -1, *out_all_pooled = 0.
  *   4. Otherwise, for each tile of tile_rows query rows (0 = all T), scores
  *      are written to `scratch` (folded mask) and the tile's top-k is taken,
- *      reusing the same scratch for every tile; *out_all_pooled = 0.  A
- *      narrow tile (<= 64 rows) over more than 32,768 pooled rows uses the
- *      chunk-parallel top-k of dsv4_topk_select_split when the scratch also
- *      holds its workspace (as dsv4_indexer_scratch_bytes sizes it), with
- *      the same result.
+ *      reusing the same scratch for every tile; *out_all_pooled = 0.  Over
+ *      more than 32,768 pooled rows the top-k runs per 32,768-column chunk
+ *      and then per row among the chunks' winners (the same result); where
+ *      k is a multiple of 4 and the first query row sees at least k pooled
+ *      rows, the chunks' winners are kept in the score rows themselves, so
+ *      the scratch does not hold the scores after the call.  Otherwise a
+ *      narrow tile (<= 64 rows) uses dsv4_topk_select_split's workspace
+ *      after the scores when the scratch holds it (as
+ *      dsv4_indexer_scratch_bytes sizes it).
  * q, w        : as dsv4_indexer_scores, T rows.
  * scratch     : device float, >= dsv4_indexer_scratch_bytes(tile, S) bytes
  *               (may be NULL on paths 2 and 3).

@@ -21,6 +21,7 @@
 #include "dsv4_device.h"
 
 static_assert(DSV4_MAX_ATTN_SPLITS == dsv4::kMaxAttnSplits, "split cap");
+static_assert(DSV4_MAX_TOPK == dsv4::kMaxTopk, "largest k: ABI and kernels agree");
 
 namespace {
 
@@ -65,9 +66,11 @@ int check_cache(const dsv4_pool_cache* c, const char* name, int need_ratio = 0) 
 
 inline int64_t vis_rows(int64_t p, int ratio = 4) { return (p + 1) / ratio; }
 
-// Chunk-parallel top-k (two passes) serves at most kSplitRows rows whose
-// visible prefixes span more than one 32,768-column chunk and hold at least
-// topk columns; its workspace is the chunk candidates' columns and scores.
+// Chunk-parallel top-k (two passes) serves rows whose visible prefixes span
+// more than one 32,768-column chunk and hold at least topk columns: at most
+// kSplitRows of them, or any number when k is a multiple of 4 and a row has
+// at most 32,768 candidates (the register kernels' two passes).  Its
+// workspace is the chunk candidates' columns and scores.
 constexpr int64_t kSplitRows = 64;
 constexpr int64_t kTopkChunk = 32768;
 
@@ -78,8 +81,9 @@ size_t split_ws_bytes(int64_t rows, int64_t chunks, int32_t topk) {
 }
 
 bool split_applies(int64_t rows, int64_t q_pos0, int32_t topk) {
-  return rows > 0 && rows <= kSplitRows && dsv4_topk_split_chunks(rows, q_pos0) >= 2 &&
-         (q_pos0 + 1) / 4 >= topk;
+  const int64_t chunks = dsv4_topk_split_chunks(rows, q_pos0);
+  return rows > 0 && chunks >= 2 && (q_pos0 + 1) / 4 >= topk &&
+         (rows <= kSplitRows || (topk % 4 == 0 && chunks * topk <= kTopkChunk));
 }
 
 // The MFMA kernels read operands with 16-byte vector loads.
@@ -298,7 +302,13 @@ int dsv4_indexer_select(const dsv4_pool_cache* index_cache, int64_t n_attn_rows,
                        scratch_bytes >= need + split_ws_bytes(rows,
                                                               dsv4_topk_split_chunks(rows, q_pos0 + t0),
                                                               topk);
-    if (split)
+    if (dsv4_topk_inplace_applies(scratch, rows, stride, q_pos0 + t0, topk))
+      // long rows: two register passes, the chunks' candidates kept in the
+      // tile's own score rows
+      rc = hip_status(dsv4_launch_topk_inplace(scratch, rows, stride, q_pos0 + t0, topk,
+                                               out_idx + t0 * topk, s),
+                      "topk launch");
+    else if (split)
       rc = launch_topk_any("indexer_select", scratch, rows, stride, q_pos0 + t0, topk,
                            out_idx + t0 * topk, reinterpret_cast<char*>(scratch) + need,
                            scratch_bytes - need, s);

@@ -63,6 +63,8 @@ __device__ __forceinline__ float relu_bits(float x) {
 // Most key splits of one query in the narrow-query attention (one wave
 // merges their states).
 constexpr int kMaxAttnSplits = 64;
+// Largest k of a selection (the ABI's DSV4_MAX_TOPK).
+constexpr int kMaxTopk = 4096;
 constexpr int64_t kMaxScoreStride = (int64_t(1) << 28) - 64;
 
 // Pooled rows visible to a query at absolute position p (ratio 4).
@@ -120,6 +122,14 @@ hipError_t dsv4_launch_indexer_scores(const void* q, const float* w, const void*
                                       int64_t out_stride, hipStream_t s);
 hipError_t dsv4_launch_topk(const float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
                             int32_t topk, int32_t* out_idx, hipStream_t s);
+// Top-k of long rows (2 to 8 chunks of 32,768 columns, k a multiple of 4,
+// every row showing at least k columns, row starts 16-byte aligned) that
+// reuses the score rows as its workspace: each chunk's candidates overwrite
+// the chunk's first 2 k floats.  The scores are not preserved.
+bool dsv4_topk_inplace_applies(const float* scores, int64_t rows, int64_t stride,
+                               int64_t q_pos0, int32_t topk);
+hipError_t dsv4_launch_topk_inplace(float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
+                                    int32_t topk, int32_t* out_idx, hipStream_t s);
 // Chunk-parallel top-k of a few long rows (two passes; see topk.hip): the
 // number of 32,768-column chunks of the longest row, and the launch, which
 // needs cand_idx / cand_score of rows * chunks * topk entries each.

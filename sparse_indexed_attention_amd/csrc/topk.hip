@@ -722,10 +722,49 @@ __device__ __forceinline__ void place_group(int v0, uint32_t& base, uint32_t spa
   }
 }
 
-template <int KPL, int NW>
+// The register kernel's passes:
+//   kRegRows:  each row's top-k of its visible prefix (the per-row selection);
+//   kRegChunk: each (row, chunk) pair, a chunk being kRegChunkCols columns of
+//              the row's visible prefix, on its own: its chosen scores and
+//              (row) columns in column order, padded with -inf / -1 to k;
+//   kRegMerge: each row's top-k of the n2 candidates of its chunks (in chunk
+//              order, so in column order), mapped back to columns.
+// Exact for the same reason as the two-pass top-k above: the top-k of a
+// union under (score desc, column asc) is the top-k of the parts' top-k,
+// and the padding is never chosen while the row shows at least k columns.
+enum RegPass { kRegRows = 0, kRegChunk = 1, kRegMerge = 2 };
+constexpr int kRegChunkCols = 8 * 64 * 64;  // one chunk: 8 waves of 4,096 columns
+
+struct RegArgs {
+  const float* scores;  // kRegRows, kRegChunk: score rows; kRegMerge: candidate scores
+  int64_t rows, stride, q_pos0;
+  int topk, cap, words;
+  int32_t* out_idx;     // kRegRows, kRegMerge
+  // kRegChunk: chunks per row.  The candidates of (row, chunk) go to
+  // cand_score / cand_col + (row * cpr + chunk) * topk; with cand_score null,
+  // into the chunk's own first 2 topk floats instead (its scores, then its
+  // columns as int32), which the chunk no longer needs once selected.
+  int cpr;
+  float* cand_score;
+  int32_t* cand_col;
+  // kRegMerge: n2 candidates per row; candidate c sits at float
+  // (c / topk) * cstride + c % topk of its row (cstride == topk: contiguous),
+  // and its column at the same offset of col_base + row * col_stride.
+  int n2;
+  int cstride;
+  const int32_t* col_base;
+  int64_t col_stride;
+  uint32_t kmagic;  // floor(2^32 / topk) + 1: c / topk == mulhi(c, kmagic) for c < 2^20
+};
+
+template <int KPL, int NW, int PASS>
 __global__ void __launch_bounds__(64 * (NW == 1 ? kShortWaves : NW), 4)
-topk_reg_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int64_t q_pos0,
-                int topk, int cap, int words, int32_t* __restrict__ out_idx) {
+topk_reg_kernel(const RegArgs a) {
+  static_assert(PASS != kRegChunk || (NW == 8 && KPL == 64), "a chunk is 8 waves of 4,096 columns");
+  const float* const __restrict__ scores = a.scores;
+  const int64_t rows = a.rows, stride = a.stride, q_pos0 = a.q_pos0;
+  const int topk = a.topk, cap = a.cap, words = a.words;
+  int32_t* const __restrict__ out_idx = a.out_idx;
   static_assert(KPL % 4 == 0 && KPL <= 64, "keys per lane");
   static_assert(NW == 1 || KPL == 64, "rows of several waves hold 4,096 columns per wave");
   constexpr int kSteps = KPL / 4;
@@ -742,12 +781,32 @@ topk_reg_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rslot = NW == 1 ? wave : 0;  // row of this wave within the workgroup
   const int wr = NW == 1 ? 0 : wave;     // part of the row held by this wave
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerWG + rslot;
-  if (row >= rows) return;  // NW > 1: the whole workgroup (one row)
+  // item: a row, or (kRegChunk) a (row, chunk) pair per workgroup
+  const int64_t item = PASS == kRegChunk ? static_cast<int64_t>(blockIdx.x)
+                                         : static_cast<int64_t>(blockIdx.x) * kRowsPerWG + rslot;
+  const int64_t row = PASS == kRegChunk ? item / a.cpr : item;
+  const int64_t chunk = PASS == kRegChunk ? item - row * a.cpr : 0;
+  if (row >= rows) return;  // NW > 1: the whole workgroup (one item)
   uint32_t* const row_lds = lds_all + rslot * words;
   uint16_t* const ob = reinterpret_cast<uint16_t*>(row_lds);
   uint32_t* const cand = cand_all[wave];
-  const int vis = static_cast<int>(visible_rows(q_pos0 + row));
+  int vis;  // the item's columns
+  if (PASS == kRegChunk) {
+    const int64_t v = visible_rows(q_pos0 + row) - chunk * kRegChunkCols;
+    vis = static_cast<int>(v < 0 ? 0 : (v > kRegChunkCols ? kRegChunkCols : v));
+  } else if (PASS == kRegMerge) {
+    vis = a.n2;
+  } else {
+    vis = static_cast<int>(visible_rows(q_pos0 + row));
+  }
+  const float* const rsrc = scores + row * stride + chunk * kRegChunkCols;
+  // float offset of item column c from rsrc (kRegMerge: candidate c's score);
+  // with topk % 4 == 0 four candidates c .. c+3 (c % 4 == 0) are adjacent
+  auto addr = [&](int c) -> int {
+    if (PASS != kRegMerge) return c;
+    const uint32_t qd = __umulhi(static_cast<uint32_t>(c), a.kmagic);
+    return static_cast<int>(qd) * a.cstride + (c - static_cast<int>(qd) * topk);
+  };
   const int need = vis < topk ? vis : topk;  // <= cap
   const int col0 = wr * kCols;
   const int nthr = 64 * NW, tid_r = 64 * wr + lane;  // threads of the row, and this one
@@ -755,6 +814,36 @@ topk_reg_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, 
   auto row_sync = [&]() {
     if (NW == 1) wave_lds_sync();
     else __syncthreads();
+  };
+  // Output of the chunk and merge passes: slot j < nsel holds item column
+  // idx(j); the other slots up to k are padding.
+  auto write_out = [&](int nsel, auto idx) {
+    if constexpr (PASS == kRegMerge) {
+      const int32_t* cb = a.col_base + row * a.col_stride;
+      for (int j = tid_r; j < topk; j += nthr) dst[j] = j < nsel ? cb[addr(idx(j))] : -1;
+    } else if constexpr (PASS == kRegChunk) {
+      // every thread reads its slots' scores first: written in place, they
+      // overwrite the chunk's first columns
+      constexpr int kPer = (kMaxTopk + 64 * NW - 1) / (64 * NW);
+      float sv[kPer];
+      int32_t cv[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int j = tid_r + u * nthr;
+        const int c = j < nsel ? idx(j) : -1;
+        sv[u] = c >= 0 ? rsrc[c] : -INFINITY;
+        cv[u] = c >= 0 ? static_cast<int32_t>(chunk * kRegChunkCols + c) : -1;
+      }
+      __syncthreads();
+      float* const os = a.cand_score ? a.cand_score + item * topk : const_cast<float*>(rsrc);
+      int32_t* const oc = a.cand_score ? a.cand_col + item * topk
+                                       : reinterpret_cast<int32_t*>(const_cast<float*>(rsrc) + topk);
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int j = tid_r + u * nthr;
+        if (j < topk) { os[j] = sv[u]; oc[j] = cv[u]; }
+      }
+    }
   };
   auto clear_hist = [&](uint32_t* h) {  // the row's threads clear kBins words
 #pragma unroll
@@ -764,7 +853,7 @@ topk_reg_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, 
   auto hist_of = [&](int pass) { return row_lds + (NW > 1 ? (pass & 1) * kBins : 0); };
 
   if (need < vis) {
-    const float* src = scores + row * stride;
+    const float* src = rsrc;
     // loads: lanes past the prefix re-read its last float4 (rows hold
     // `stride` >= vis floats with stride % 4 == 0, so that float4 is in
     // bounds); their keys are cleared below.  A wave wholly past the prefix
@@ -775,7 +864,7 @@ topk_reg_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, 
 #pragma unroll
       for (int v = 0; v < kSteps; ++v) {
         const int c = col0 + 256 * v + 4 * lane;
-        x[v] = *reinterpret_cast<const float4*>(src + (c < clast ? c : clast));
+        x[v] = *reinterpret_cast<const float4*>(src + addr(c < clast ? c : clast));
       }
     } else {
 #pragma unroll
@@ -1038,7 +1127,9 @@ topk_reg_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, 
       }
     }
     row_sync();
-    if ((topk & 3) == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+    if constexpr (PASS != kRegRows) {
+      write_out(need, [&](int j) { return static_cast<int>(ob[j]); });
+    } else if ((topk & 3) == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
       for (int j = 4 * tid_r; j < topk; j += 4 * nthr) {
         uint2 w = make_uint2(0u, 0u);
         if (j < need) w = *reinterpret_cast<const uint2*>(&ob[j]);  // inside the row's slots
@@ -1058,53 +1149,105 @@ topk_reg_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, 
     }
   } else {
     // every visible column is chosen
-    for (int j = tid_r; j < topk; j += nthr) dst[j] = j < need ? j : -1;
+    if constexpr (PASS != kRegRows) write_out(need, [&](int j) { return j; });
+    else for (int j = tid_r; j < topk; j += nthr) dst[j] = j < need ? j : -1;
   }
 }
 
 // Longest row the register-resident kernels take (8 waves of 4,096 columns).
-constexpr int64_t kRegMaxVis = 8 * 64 * 64;
+constexpr int64_t kRegMaxVis = kRegChunkCols;
 
-hipError_t launch_reg(const float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
-                      int32_t topk, int32_t* out_idx, hipStream_t s) {
-  const int64_t max_vis = (q_pos0 + rows) / 4;
-  const int cap = static_cast<int>(max_vis < topk ? max_vis : topk);  // chosen slots per row
-  if (max_vis <= 64 * 64) {
-    // one wave per row, kShortWaves rows per workgroup; per wave the
+// One pass of the register kernel over items of at most max_cols columns
+// (kRegChunk: chunks of kRegChunkCols); a.cap and a.words are set here.
+template <int PASS>
+hipError_t launch_reg(RegArgs a, int64_t max_cols, hipStream_t s) {
+  const int64_t items = PASS == kRegChunk ? a.rows * a.cpr : a.rows;
+  a.cap = static_cast<int>(max_cols < a.topk ? max_cols : a.topk);  // chosen slots per item
+  if (PASS != kRegChunk && max_cols <= 64 * 64) {
+    // one wave per item, kShortWaves items per workgroup; per wave the
     // histogram, later the chosen columns + 64 spare slots (16-bit)
-    const dim3 grid(static_cast<unsigned>((rows + kShortWaves - 1) / kShortWaves));
+    const dim3 grid(static_cast<unsigned>((items + kShortWaves - 1) / kShortWaves));
     const dim3 block(64 * kShortWaves);
-    int words = (cap + 64 + 1) / 2;
+    int words = (a.cap + 64 + 1) / 2;
     if (words < kBins) words = kBins;
-    words = (words + 3) & ~3;
-    const size_t lds = static_cast<size_t>(kShortWaves) * words * sizeof(uint32_t);
-    if (max_vis <= 1024)
-      hipLaunchKernelGGL((topk_reg_kernel<16, 1>), grid, block, lds, s, scores, rows, stride,
-                         q_pos0, topk, cap, words, out_idx);
-    else if (max_vis <= 2048)
-      hipLaunchKernelGGL((topk_reg_kernel<32, 1>), grid, block, lds, s, scores, rows, stride,
-                         q_pos0, topk, cap, words, out_idx);
+    a.words = (words + 3) & ~3;
+    const size_t lds = static_cast<size_t>(kShortWaves) * a.words * sizeof(uint32_t);
+    constexpr int P1 = PASS == kRegChunk ? kRegRows : PASS;  // (never a chunk pass here)
+    if (max_cols <= 1024)
+      hipLaunchKernelGGL((topk_reg_kernel<16, 1, P1>), grid, block, lds, s, a);
+    else if (max_cols <= 2048)
+      hipLaunchKernelGGL((topk_reg_kernel<32, 1, P1>), grid, block, lds, s, a);
     else
-      hipLaunchKernelGGL((topk_reg_kernel<64, 1>), grid, block, lds, s, scores, rows, stride,
-                         q_pos0, topk, cap, words, out_idx);
+      hipLaunchKernelGGL((topk_reg_kernel<64, 1, P1>), grid, block, lds, s, a);
     return hipGetLastError();
   }
-  // one row per workgroup of NW waves; two histograms per row, later the
+  // one item per workgroup of NW waves; two histograms per item, later the
   // chosen columns + 64 spare slots per wave (cap + 64 NW <= 4,608 16-bit
   // slots, inside the 2 x kBins words)
-  const int words = 2 * kBins;
-  const size_t lds = static_cast<size_t>(words) * sizeof(uint32_t);
-  const dim3 grid(static_cast<unsigned>(rows));
-  if (max_vis <= 2 * 64 * 64)
-    hipLaunchKernelGGL((topk_reg_kernel<64, 2>), grid, dim3(128), lds, s, scores, rows, stride,
-                       q_pos0, topk, cap, words, out_idx);
-  else if (max_vis <= 4 * 64 * 64)
-    hipLaunchKernelGGL((topk_reg_kernel<64, 4>), grid, dim3(256), lds, s, scores, rows, stride,
-                       q_pos0, topk, cap, words, out_idx);
+  a.words = 2 * kBins;
+  const size_t lds = static_cast<size_t>(a.words) * sizeof(uint32_t);
+  const dim3 grid(static_cast<unsigned>(items));
+  constexpr int P2 = PASS == kRegChunk ? kRegRows : PASS;  // chunk items take 8 waves
+  if (PASS == kRegChunk || max_cols > 4 * 64 * 64)
+    hipLaunchKernelGGL((topk_reg_kernel<64, 8, PASS>), grid, dim3(512), lds, s, a);
+  else if (max_cols > 2 * 64 * 64)
+    hipLaunchKernelGGL((topk_reg_kernel<64, 4, P2>), grid, dim3(256), lds, s, a);
   else
-    hipLaunchKernelGGL((topk_reg_kernel<64, 8>), grid, dim3(512), lds, s, scores, rows, stride,
-                       q_pos0, topk, cap, words, out_idx);
+    hipLaunchKernelGGL((topk_reg_kernel<64, 2, P2>), grid, dim3(128), lds, s, a);
   return hipGetLastError();
+}
+
+RegArgs reg_args(const float* scores, int64_t rows, int64_t stride, int64_t q_pos0, int32_t topk,
+                 int32_t* out_idx) {
+  RegArgs a{};
+  a.scores = scores;
+  a.rows = rows;
+  a.stride = stride;
+  a.q_pos0 = q_pos0;
+  a.topk = topk;
+  a.out_idx = out_idx;
+  return a;
+}
+
+// Whether the two register passes (chunks, then merge) serve these rows:
+// row starts 16-byte aligned, k a multiple of 4 (the merge reads candidates
+// four at a time), every row showing at least k columns (the padding is
+// never chosen), at most 32,768 candidates per row, and, in place, room for
+// the last chunk's 2 k candidate floats inside the row.
+bool reg_split_ok(const float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
+                  int32_t topk, bool in_place) {
+  if (rows <= 0 || (stride & 3) != 0 || (reinterpret_cast<uintptr_t>(scores) & 15) != 0 ||
+      (topk & 3) != 0)
+    return false;
+  const int64_t max_vis = (q_pos0 + rows) / 4;
+  const int64_t cpr = (max_vis + kRegChunkCols - 1) / kRegChunkCols;
+  if (cpr < 2 || cpr * topk > kRegMaxVis || (q_pos0 + 1) / 4 < topk) return false;
+  return !in_place || (cpr - 1) * kRegChunkCols + 2 * static_cast<int64_t>(topk) <= stride;
+}
+
+// The two register passes; candidates in cand_score / cand_col (rows * cpr *
+// topk each), or in place in the score rows when cand_score is null.
+hipError_t launch_reg_split(const float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
+                            int32_t topk, int32_t* out_idx, float* cand_score, int32_t* cand_col,
+                            hipStream_t s) {
+  const int64_t max_vis = (q_pos0 + rows) / 4;
+  const int cpr = static_cast<int>((max_vis + kRegChunkCols - 1) / kRegChunkCols);
+  RegArgs a1 = reg_args(scores, rows, stride, q_pos0, topk, nullptr);
+  a1.cpr = cpr;
+  a1.cand_score = cand_score;
+  a1.cand_col = cand_col;
+  hipError_t e = launch_reg<kRegChunk>(a1, kRegChunkCols, s);
+  if (e != hipSuccess) return e;
+  const int n2 = cpr * topk;
+  const bool in_place = cand_score == nullptr;
+  RegArgs a2 = reg_args(in_place ? scores : cand_score, rows, in_place ? stride : n2, q_pos0,
+                        topk, out_idx);
+  a2.n2 = n2;
+  a2.cstride = in_place ? kRegChunkCols : topk;
+  a2.col_base = in_place ? reinterpret_cast<const int32_t*>(scores) + topk : cand_col;
+  a2.col_stride = in_place ? stride : n2;
+  a2.kmagic = static_cast<uint32_t>((uint64_t(1) << 32) / static_cast<uint64_t>(topk) + 1);
+  return launch_reg<kRegMerge>(a2, n2, s);
 }
 
 template <int CPT, int PER>
@@ -1152,8 +1295,9 @@ hipError_t dsv4_launch_topk(const float* scores, int64_t rows, int64_t stride, i
                             int32_t topk, int32_t* out_idx, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   const bool aligned = (stride & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
-  if (aligned && (q_pos0 + rows) / 4 <= kRegMaxVis)
-    return launch_reg(scores, rows, stride, q_pos0, topk, out_idx, s);
+  const int64_t max_vis = (q_pos0 + rows) / 4;
+  if (aligned && max_vis <= kRegMaxVis)
+    return launch_reg<kRegRows>(reg_args(scores, rows, stride, q_pos0, topk, out_idx), max_vis, s);
   return launch_rows(scores, rows, stride, q_pos0, topk, out_idx, -1, nullptr, s);
 }
 
@@ -1168,6 +1312,9 @@ hipError_t dsv4_launch_topk_split(const float* scores, int64_t rows, int64_t str
   if (rows <= 0) return hipSuccess;
   const int64_t cpr = dsv4_topk_split_chunks(rows, q_pos0);
   if (cpr < 1 || cpr * topk > (int64_t(1) << 30)) return hipErrorInvalidValue;
+  static_assert(kSplitChunk == kRegChunkCols, "both two-pass top-k use the same chunks");
+  if (reg_split_ok(scores, rows, stride, q_pos0, topk, false))
+    return launch_reg_split(scores, rows, stride, q_pos0, topk, out_idx, cand_score, cand_idx, s);
   // pass 1: every (row, chunk) item on its own, as many workgroups as items
   // (at most one per CU, persistent)
   const int64_t items = rows * cpr;
@@ -1186,4 +1333,16 @@ hipError_t dsv4_launch_topk_split(const float* scores, int64_t rows, int64_t str
   // pass 2: top-k of each row's cpr * topk candidates, mapped back to columns
   const int64_t n2 = cpr * topk;
   return launch_rows(cand_score, rows, n2, q_pos0, topk, out_idx, n2, cand_idx, s);
+}
+
+bool dsv4_topk_inplace_applies(const float* scores, int64_t rows, int64_t stride,
+                               int64_t q_pos0, int32_t topk) {
+  return reg_split_ok(scores, rows, stride, q_pos0, topk, true);
+}
+
+hipError_t dsv4_launch_topk_inplace(float* scores, int64_t rows, int64_t stride, int64_t q_pos0,
+                                    int32_t topk, int32_t* out_idx, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (!reg_split_ok(scores, rows, stride, q_pos0, topk, true)) return hipErrorInvalidValue;
+  return launch_reg_split(scores, rows, stride, q_pos0, topk, out_idx, nullptr, nullptr, s);
 }

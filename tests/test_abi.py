@@ -176,7 +176,12 @@ def test_split_topk_sizing_and_gates():
     # 1 row at position 2^20 - 4: 262,143 visible -> 8 chunks of 32,768
     assert ws(1, (1 << 20) - 4, 2048) == 2 * 8 * 2048 * 4
     assert ws(3, (1 << 20) - 4, 7) == 2 * ((3 * 8 * 7 * 4 + 15) // 16 * 16)
-    assert ws(65, (1 << 20) - 4, 2048) == 0           # too many rows: per-row kernel
+    assert ws(65, (1 << 20) - 4, 7) == 0              # too many rows for odd k: per-row kernel
+    # whole tiles (last row sees 262,144 columns: 8 chunks) when k % 4 == 0 and
+    # a row has at most 32,768 candidates
+    assert ws(1024, (1 << 20) - 1024, 2048) == 2 * 1024 * 8 * 2048 * 4
+    assert ws(65, (1 << 20) - 65, 4096) == 2 * 65 * 8 * 4096 * 4
+    assert ws(65, (1 << 20) - 60, 4096) == 0          # 9 chunks x 4,096 candidates: too many
     assert ws(1, 4 * 32767, 2048) == 0                # one chunk
     # narrow tiles over long rows get room for the split top-k (sized for k = 4096)
     assert dsv4.dsv4_indexer_scratch_bytes(1, 262144) == 262144 * 4 + 2 * 8 * 4096 * 4

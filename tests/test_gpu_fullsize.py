@@ -58,11 +58,18 @@ def check_chunk(cs: ChunkState, tile: int, n_random: int, n_attn: int):
     np.testing.assert_array_equal(cs.acache.rows[S - n_new:S].float().cpu().numpy(),
                                   cs.oracle_pooled()[S - n_new:S])
     tile_rows = T if tile == 0 else tile
-    last_t0 = (T - 1) // tile_rows * tile_rows       # scratch holds the last tile
+    last_t0 = (T - 1) // tile_rows * tile_rows
     rows = sample_rows(T, tile_rows, n_random)
     keys = cs.oracle_keys()
     gidx = idx.cpu().numpy()
-    g_scr = scratch.cpu().numpy()
+    # the last tile's scores, recomputed (the score kernel is deterministic):
+    # over rows longer than 32,768 columns the select keeps its chunk
+    # candidates in the scratch's score rows
+    last = torch.empty((T - last_t0, dsv4.dsv4_score_stride(S)), device="cuda")
+    dsv4.dsv4_indexer_scores(cs.icache, cs.q_idx[last_t0:].contiguous(),
+                             cs.w[last_t0:].contiguous(), cs.q_pos0 + last_t0, last)
+    torch.cuda.synchronize()
+    g_scr = last.cpu().numpy()
     for t in rows:
         ref = O.indexer_scores(cs.inp["q_idx"][t:t + 1], cs.inp["w"][t:t + 1], keys,
                                cs.q_pos0 + t, S)

@@ -162,6 +162,23 @@ def test_split_topk_equals_per_row_kernel(rows, q_pos0, kind, topk):
     np.testing.assert_array_equal(a, b)
 
 
+@pytest.mark.parametrize("rows,q_pos0,topk", [(300, 4 * 70000, 2048), (130, 4 * 40000, 4096),
+                                              (1024, (1 << 20) - 1024, 2048)])
+@pytest.mark.parametrize("kind", ["normal", "ties"])
+def test_split_topk_many_rows_equals_per_row_kernel(rows, q_pos0, topk, kind):
+    """More than 64 rows take the two-pass top-k when k % 4 == 0 and a row has
+    at most 32,768 chunk candidates (whole tiles at 1M context included); the
+    result is the per-row kernel's, and sampled rows are the oracle's."""
+    s = _scores(kind, rows, q_pos0, seed=rows + topk)
+    a, b, nb = _topk_both(s, q_pos0, topk)
+    assert nb > 0
+    np.testing.assert_array_equal(a, b)
+    rng = np.random.default_rng(rows)
+    for t in rng.choice(rows, 6, replace=False):
+        vis = O.visible_rows(q_pos0 + int(t))
+        np.testing.assert_array_equal(a[t], O.topk_row(s[t].astype(np.float64), vis, topk))
+
+
 @pytest.mark.parametrize("kind", ["normal", "ties"])
 def test_split_topk_matches_oracle(kind):
     rows, q_pos0, topk = 2, 4 * 70000, 2048        # 3 chunks, the last one short
@@ -171,24 +188,32 @@ def test_split_topk_matches_oracle(kind):
     np.testing.assert_array_equal(a, O.topk_select(s.astype(np.float64), q_pos0, topk))
 
 
-def test_narrow_select_split_path_equals_per_row_path_and_oracle():
-    """T = 3 query rows at ~140K tokens (35,000 pooled rows, 2 chunks): the
-    indexer select with the scratch dsv4_indexer_scratch_bytes sizes (the
-    chunk-parallel top-k) against the same call with only the score rows
-    (the per-row top-k), and against the oracle."""
+@pytest.mark.parametrize("T,S_tokens,topk", [(3, 140000, 512), (64, 4 * 70000, 2048),
+                                            (200, 4 * 40000, 512)])
+def test_select_long_rows_equals_per_row_kernel_and_oracle(T, S_tokens, topk):
+    """Indexer select over rows longer than one 32,768-column chunk (2 or 3
+    chunks): its top-k runs in two register passes whose chunk candidates are
+    kept in the tile's own score rows.  It must equal the LDS-staged per-row
+    kernel on the same GPU scores (computed separately and kept), with the
+    scratch dsv4_indexer_scratch_bytes sizes and with only the score rows, and
+    the oracle's selection from the oracle's scores."""
     from test_gpu_parity import _score_case
     from parity_util import assert_selection_matches
-    T, topk = 3, 512
-    c, st, S, q_pos0, q, w = _score_case(T, 140000, T, 64, 128, seed=8)
+    c, st, S, q_pos0, q, w = _score_case(T, S_tokens, T, 64, 128, seed=T + 8)
     assert S > 32768
     qd, wd = bf16_t(q).cuda(), torch.from_numpy(w).cuda()
+    stride = dsv4.dsv4_score_stride(S)
+    sc = torch.empty((T, stride), device="cuda")
+    dsv4.dsv4_indexer_scores(c, qd, wd, q_pos0, sc)
+    per_row = torch.empty((T, topk), dtype=torch.int32, device="cuda")
+    dsv4.dsv4_topk_select(sc, q_pos0, S, topk, per_row)
     outs = []
-    for nbytes in (dsv4.dsv4_indexer_scratch_bytes(T, S), T * dsv4.dsv4_score_stride(S) * 4):
+    for nbytes in (dsv4.dsv4_indexer_scratch_bytes(T, S), T * stride * 4):
         scratch = torch.empty(nbytes // 4, device="cuda")
         out = torch.full((T, topk), 5, dtype=torch.int32, device="cuda")
         assert not dsv4.dsv4_indexer_select(c, S, qd, wd, T, q_pos0, 64, topk, out, scratch, 0)
         outs.append(out)
     torch.cuda.synchronize()
-    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(outs[0], per_row) and torch.equal(outs[1], per_row)
     ref = O.indexer_scores(q, w, st.rows[:S], q_pos0, S)
     assert_selection_matches(outs[0].cpu().numpy(), ref, q_pos0, topk)
