@@ -388,6 +388,11 @@ def tile_matrix(steps: int):
         if n_tiles > 1:
             bufs.append(torch.empty(st.tile * stride, device="cuda").view(st.tile, stride))
         main, aux = torch.cuda.current_stream(), torch.cuda.Stream()
+        # the top-k the select runs: the two-pass chunk top-k over long rows,
+        # here with a workspace per buffer (the select keeps the chunk winners
+        # in its scratch, but a ping-pong buffer is rescored while its top-k runs)
+        nb_ws = d.dsv4_topk_split_workspace_bytes(st.tile, q0 + T - st.tile, wl.topk)
+        wss = [torch.empty(nb_ws // 4, device="cuda") if nb_ws else None for _ in bufs]
 
         def serial():
             d.dsv4_indexer_select(st.icache, st.acache.n_rows, st.q_idx, st.w, T, q0,
@@ -407,8 +412,12 @@ def tile_matrix(steps: int):
                                       bufs[b][:n], True, stream=main)
                 ev_sc[b].record(main)
                 aux.wait_event(ev_sc[b])
-                d.dsv4_topk_select(bufs[b][:n], q0 + t0, S, wl.topk, st.idx[t0:t0 + n],
-                                   stream=aux)
+                if nb_ws:
+                    d.dsv4_topk_select_split(bufs[b][:n], q0 + t0, S, wl.topk, st.idx[t0:t0 + n],
+                                             wss[b], stream=aux)
+                else:
+                    d.dsv4_topk_select(bufs[b][:n], q0 + t0, S, wl.topk, st.idx[t0:t0 + n],
+                                       stream=aux)
                 ev_tk[b].record(aux)
             for e in ev_tk:
                 main.wait_event(e)
@@ -425,12 +434,13 @@ def tile_matrix(steps: int):
         one = d.dsv4_indexer_scratch_bytes(st.tile, S)
         print(json.dumps({
             "workload": wl.name, "context_tokens": q0 + T, "chunk": T, "tile_rows": st.tile,
-            "pooled_rows": S, "scratch_bytes": one, "pingpong_scratch_bytes": one * len(bufs),
+            "pooled_rows": S, "scratch_bytes": one,
+            "pingpong_scratch_bytes": (one + nb_ws) * len(bufs),
             "select_ms": ms_serial, "select_rows_per_s": T / (ms_serial * 1e-3),
             "pingpong_select_ms": ms_pp, "pingpong_equal_selection": same,
             "step_ms": ms_step, "step_rows_per_s": T / (ms_step * 1e-3)}))
         sys.stdout.flush()
-        del st, bufs
+        del st, bufs, wss
         torch.cuda.empty_cache()
 
 
