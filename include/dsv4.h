@@ -43,7 +43,9 @@
 extern "C" {
 #endif
 
-#define DSV4_ABI_VERSION 3
+/* 4: dsv4_indexer_select may keep top-k candidates in its scratch (the
+ * scores are not left there), and dsv4_topk_select_split takes more rows. */
+#define DSV4_ABI_VERSION 4
 
 /* Return codes. */
 #define DSV4_OK                0
