@@ -640,18 +640,23 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
 }
 
 // ---------------------------------------------------------------------------
-// Short rows (at most 64 * KPL visible columns): one wave per row, no
-// workgroup barriers.  The same selection rule as above, laid out for rows
-// that one wave can hold in registers:
-//   * lane L holds the float4 at columns 256v + 4L .. 256v + 4L + 3 for
-//     v = 0 .. KPL/4 - 1 (each load instruction reads 1 KiB contiguous), as
-//     keys key[4v + i]; columns past the visible prefix get key 0, and only
-//     the steps v that reach past it test for that (a wave-uniform branch);
+// Rows held in registers (at most 32,768 visible columns): one wave per row
+// up to 64 * KPL <= 4,096 columns (kShortWaves rows per workgroup, no
+// workgroup barriers), else NW = 2, 4 or 8 waves of 4,096 columns each.  The
+// same selection rule as above:
+//   * lane L holds the float4 at columns 256v + 4L .. 256v + 4L + 3 of its
+//     wave's block for v = 0 .. KPL/4 - 1 (each load instruction reads 1 KiB
+//     contiguous), as keys key[4v + i]; columns past the visible prefix get
+//     key 0, and only the steps v that reach past it test for that (a
+//     wave-uniform branch);
 //   * threshold: MSB-first radix select with 11-bit digits over a 2,048-bin
-//     LDS histogram private to the wave, from the highest bit in which the
-//     row's keys differ (wave OR of the keys and of their complements); once
-//     the bin holding the k-th key has at most 64 keys they are listed, one
-//     per lane, and ballot counts settle the remaining bits one at a time;
+//     LDS histogram (private to the wave, or shared by the row's waves and
+//     double-buffered), from the highest bit in which the row's keys differ
+//     (OR of the keys and of their complements); once the bin holding the
+//     k-th key has at most 64 keys they are listed, one per lane, and ballot
+//     counts settle the remaining bits one at a time.  Waves of one row
+//     exchange the ORs, list counts and chosen counts through LDS; every
+//     wave searches the same table, so all take the same branches;
 //   * list building and ordered emission give each key its place with one
 //     packed wave scan per three steps (10-bit per-step counts), and every
 //     key makes one unconditional LDS write, to its slot or to a slot of its
@@ -660,6 +665,7 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
 //     simply key >= T; otherwise equal keys go to the lower columns.  The
 //     chosen columns, ascending, are then copied to the output row, padded
 //     with -1 to k.
+// Longer rows run two passes of the same kernel (see RegPass below).
 constexpr int kShortWaves = 4;  // waves (rows in flight) per workgroup
 
 // Orders this wave's earlier LDS accesses before its later ones, across lanes.
