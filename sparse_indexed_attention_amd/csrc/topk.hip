@@ -8,7 +8,13 @@
 // to the lower column (-0 == +0), chosen columns written in ascending order,
 // then -1.
 //
-// HBM-bound: every visible score is read once.  Design:
+// HBM-bound: every visible score is read once.  Two kernels:
+//   * topk_reg_kernel (below, after topk_kernel) keeps a row's keys in
+//     registers: rows of up to 32,768 columns whose starts are 16-byte
+//     aligned, and, in two passes, longer rows;
+//   * topk_kernel stages rows through LDS: longer rows when there is no
+//     workspace for two passes, and any stride.
+// topk_kernel's design:
 //   * Persistent workgroups (one per CU, 16 waves) walk a list of work items,
 //     an item being a row or, for rows longer than one chunk, a chunk of a
 //     row.  The next item is copied from HBM into an LDS row buffer with
