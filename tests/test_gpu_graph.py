@@ -84,3 +84,44 @@ def test_step_graph_replays_match_eager(narrow):
         assert torch.equal(idx, want[0]), r
         assert torch.equal(out, want[1]), r
         assert torch.equal(ic.rows, want[2]) and torch.equal(ac.rows, want[3]), r
+
+
+def test_long_row_select_graph_replays_match_eager():
+    """The indexer select over rows longer than one 32,768-column chunk (the
+    score kernel, then the two register top-k passes with the chunks' winners
+    kept in the scratch) captured once and replayed, with the outputs and the
+    scratch clobbered by eager work between replays."""
+    T, S, topk = 64, 70000, 2048
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    ic = dsv4.PoolCache(S, 128)
+    ic.rows.copy_((torch.randn(S, 128, device="cuda", generator=gen) * 0.5).to(torch.bfloat16))
+    ic.set_state(S)
+    q_pos0 = 4 * S - T
+    q = torch.randn(T, 64, 128, device="cuda", generator=gen).to(torch.bfloat16)
+    w = torch.rand(T, 64, device="cuda", generator=gen)
+    scratch = torch.empty(dsv4.dsv4_indexer_scratch_bytes(T, S) // 4, device="cuda")
+    idx = torch.empty((T, topk), dtype=torch.int32, device="cuda")
+
+    def step():
+        assert not dsv4.dsv4_indexer_select(ic, S, q, w, T, q_pos0, 64, topk, idx, scratch, 0)
+
+    step()
+    torch.cuda.synchronize()
+    want = idx.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        idx.fill_(-7)
+        scratch.fill_(float(r) - 1.5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, want), r
