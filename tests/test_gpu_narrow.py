@@ -189,7 +189,10 @@ def test_split_topk_matches_oracle(kind):
 
 
 @pytest.mark.parametrize("T,S_tokens,topk", [(3, 140000, 512), (64, 4 * 70000, 2048),
-                                            (200, 4 * 40000, 512)])
+                                            (200, 4 * 40000, 512),
+                                            # the last chunk's 2k candidates do not fit
+                                            # the row: workspace split or per-row kernel
+                                            (3, 140000, 2048), (100, 140000, 2048)])
 def test_select_long_rows_equals_per_row_kernel_and_oracle(T, S_tokens, topk):
     """Indexer select over rows longer than one 32,768-column chunk (2 or 3
     chunks): its top-k runs in two register passes whose chunk candidates are
