@@ -169,3 +169,62 @@ def test_register_rows_unaligned_output(max_vis):
     assert int(flat[0]) == 77                 # nothing written before the block
     np.testing.assert_array_equal(out.cpu().numpy(),
                                   O.topk_select(s.astype(np.float64), q_pos0, topk))
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_shapes_match_oracle(case):
+    """Seeded random shapes across every top-k path: row counts, positions
+    (visible prefixes from a few columns up to three 32,768-column chunks),
+    k (odd or a multiple of 4, below or above the visible count), aligned or
+    unaligned strides, and tie-prone or continuous values; both the per-row
+    entry point and the two-pass one (with its workspace) against the oracle."""
+    rng = np.random.default_rng(1000 + case)
+    rows = int(rng.integers(1, 40))
+    max_vis = int(rng.choice([int(rng.integers(4, 600)), int(rng.integers(600, 4200)),
+                              int(rng.integers(4200, 33000)), int(rng.integers(33000, 72000))]))
+    q_pos0 = max(0, 4 * max_vis - rows)
+    n_cols = (q_pos0 + rows) // 4
+    topk = int(rng.choice([int(rng.integers(1, 9)), 4 * int(rng.integers(1, 400)),
+                           int(rng.integers(1, 4097))]))
+    stride = n_cols + int(rng.choice([0, (-n_cols) % 4, 1, 7]))
+    kind = rng.choice(["relu_sum", "levels40", "normal"])
+    s = _rows(str(kind), rows, max(n_cols, 1), rng)[:, :n_cols]
+    got, buf = _select(s, q_pos0, n_cols, topk, stride=max(stride, 1))
+    want = O.topk_select(buf.astype(np.float64), q_pos0, topk)
+    np.testing.assert_array_equal(got, want)
+    # the two-pass entry point on the same buffer
+    d = torch.from_numpy(buf).cuda()
+    nb = dsv4.dsv4_topk_split_workspace_bytes(rows, q_pos0, topk)
+    ws = torch.empty(max(nb // 4, 4), dtype=torch.float32, device="cuda")
+    out = torch.full((rows, topk), 55, dtype=torch.int32, device="cuda")
+    dsv4.dsv4_topk_select_split(d, q_pos0, n_cols, topk, out, ws if nb else None)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_long_rows_two_pass_match_oracle(case):
+    """Seeded random long rows (2 or 3 chunks of 32,768 columns) with aligned
+    strides and k % 4 == 0, so that the two register passes run: the per-row
+    entry point (LDS-staged kernel) and the two-pass one with its workspace,
+    at row counts on both sides of 64, against the oracle."""
+    rng = np.random.default_rng(2000 + case)
+    rows = int(rng.integers(1, 90))
+    max_vis = int(rng.integers(33000, 72000))
+    q_pos0 = 4 * max_vis - rows
+    n_cols = (q_pos0 + rows) // 4
+    topk = 4 * int(rng.integers(1, 1025))
+    stride = n_cols + (-n_cols) % 4 + 4 * int(rng.integers(0, 3))
+    kind = str(rng.choice(["relu_sum", "levels40", "normal"]))
+    s = _rows(kind, rows, n_cols, rng)
+    got, buf = _select(s, q_pos0, n_cols, topk, stride=stride)
+    want = O.topk_select(buf.astype(np.float64), q_pos0, topk)
+    np.testing.assert_array_equal(got, want)
+    d = torch.from_numpy(buf).cuda()
+    nb = dsv4.dsv4_topk_split_workspace_bytes(rows, q_pos0, topk)
+    assert nb > 0
+    ws = torch.empty(nb // 4, dtype=torch.float32, device="cuda")
+    out = torch.full((rows, topk), 55, dtype=torch.int32, device="cuda")
+    dsv4.dsv4_topk_select_split(d, q_pos0, n_cols, topk, out, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), want)
