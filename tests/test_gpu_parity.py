@@ -407,3 +407,32 @@ def test_attention_unsorted_and_duplicate_selections():
     torch.cuda.synchronize()
     ref = O.sparse_prefill_attention(q, q_pos0, raw, raw_pos0, W, pooled, sel, 1 / math.sqrt(D))
     assert np.abs(out.float().cpu().numpy() - ref).max() <= ATTN_ATOL
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_attention_random_shapes_match_oracle(case):
+    """Seeded random attention shapes: heads (1-64, partial head tiles), head
+    dims 32-512, windows 1-256, k 1-600, positions from the first tokens to a
+    few thousand, selections with empty and invisible slots; the per-query
+    kernel and the key-split path (random split count) against the oracle."""
+    rng = np.random.default_rng(3000 + case)
+    T = int(rng.integers(1, 24))
+    H = int(rng.choice([1, 7, 16, 33, 64]))
+    D = int(rng.choice([32, 64, 128, 256, 512]))
+    W = int(rng.choice([1, 16, 128, 256]))
+    topk = int(rng.choice([1, 8, 64, 600]))
+    q_pos0 = int(rng.choice([0, 5, int(rng.integers(40, 600)), int(rng.integers(600, 5000))]))
+    cache, pooled, raw, raw_pos0, q, sel = _attn_case(T, q_pos0, H, D, W, topk, seed=4000 + case)
+    qd = bf16_t(q.reshape(T, H * D)).cuda().view(T, H, D)
+    rawd, seld = bf16_t(raw).cuda(), torch.from_numpy(sel).cuda()
+    ref = O.sparse_prefill_attention(q, q_pos0, raw, raw_pos0, W, pooled, sel, 1 / math.sqrt(D))
+    out = torch.zeros((T, H, D), dtype=torch.bfloat16, device="cuda")
+    dsv4.dsv4_sparse_prefill_attn(qd, q_pos0, rawd, raw_pos0, W, cache, seld, out)
+    ns = int(rng.integers(1, 9))
+    ws = torch.empty(T * ns * H * (D + 2), device="cuda")  # (m, l, O) of every split
+    out2 = torch.zeros((T, H, D), dtype=torch.bfloat16, device="cuda")
+    dsv4.dsv4_sparse_attn_narrow(qd, q_pos0, rawd, raw_pos0, W, cache, seld, out2, ns, ws)
+    torch.cuda.synchronize()
+    for o in (out, out2):
+        err = np.abs(o.float().cpu().numpy() - ref).max()
+        assert err <= ATTN_ATOL, (case, err)
