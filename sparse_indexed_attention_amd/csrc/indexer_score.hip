@@ -42,13 +42,14 @@
 //   * Four-wave workgroups, two per CU: their barriers are independent, so one
 //     workgroup's epilogue VALU work overlaps the other's MFMAs.
 //   * Grid: workgroups are dealt round-robin to the 8 XCDs, and blockIdx % 8
-//     picks the XCD's share: with enough query blocks, XCD x takes query
-//     group x / 4 (every other query block) and column group x % 4 (a quarter
-//     of the key rows, 2 MiB at 128K context, resident in that XCD's 4 MiB
-//     L2), so each query block's q is fetched by 4 XCDs and each key row by
-//     2; with few query blocks every XCD takes all of them and an eighth of
-//     the columns.  Score rows are written non-temporal so the stream of
-//     output does not evict the keys from L2.
+//     picks the XCD's share, one of query groups x column groups = 8.  XCD x
+//     takes query group x / cgroups (every qgroups-th query block) and column
+//     group x % cgroups (that fraction of the key rows, which stays in the
+//     XCD's 4 MiB L2 while the XCD works through it), so each query block's
+//     q is fetched by cgroups XCDs and each key row by qgroups.  The launch
+//     picks cgroups to balance those two fetches.  Score rows are written
+//     non-temporal so the stream of output does not evict the keys from L2.
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -337,24 +338,32 @@ hipError_t launch_t(const void* q, const float* w, const void* keys, int64_t row
                     int64_t q_pos0, int64_t S, int n_heads, int fold_mask, float* out,
                     int64_t out_stride, hipStream_t s) {
   const int64_t nqb = (rows + kQB - 1) / kQB;
+  const int64_t tiles = (S + kTileCols - 1) / kTileCols;
+  // Column splits over the whole key range: as few as fill one round of two
+  // workgroups per CU (512), and at most 256 tiles (16,384 key rows) each.
+  // Every workgroup stages its 8 queries (128 KiB at 64 heads x 128) before
+  // its first tile, so longer splits amortise that; a second round would
+  // load new queries into the L2 that holds the keys and fetch the keys
+  // again (at 128K, 2,048 rows: 106 MB per launch in one round, 154 MB in 8,
+  // same time).  Past 256 tiles per split, rounds even out the CUs instead
+  // (at 1M context one round of 512 takes 4% longer than 4,096 workgroups).
+  int64_t sp = std::max<int64_t>((512 + nqb - 1) / nqb, (tiles + 255) / 256);
+  sp = std::min<int64_t>(sp, tiles);
+  if (sp < 1) sp = 1;
   // XCD shares: query groups x column groups = 8 (see the kernel comment).
-  const int cgroups = nqb >= 16 ? 4 : 8;
+  // An XCD reads S / cgroups key rows and nqb * cgroups / 8 query blocks, so
+  // key bytes + query bytes is least near cgroups^2 = S / (nqb * n_heads);
+  // take the power of two nearest that, at most 8 and at most sp.
+  int cgroups = 8;
+  while (cgroups > 1 &&
+         (cgroups > sp || static_cast<int64_t>(cgroups) * cgroups * nqb * n_heads > 2 * S))
+    cgroups >>= 1;
   const int64_t qgroups = 8 / cgroups;
   const int64_t nqb_g = (nqb + qgroups - 1) / qgroups;  // query blocks per query group
-  // Column splits per column group.  Every workgroup re-reads its queries
-  // and runs a pipeline prologue, so for few query blocks more, shorter
-  // splits lose (at 64 query rows, 4,096 one-tile splits take twice as long
-  // as 256 long ones): about two workgroups per CU in all (512) below 32
-  // query blocks, four (1,024) below 128.  From 128 blocks (1,024 rows) the
-  // splits are long anyway and 4,096 workgroups keep the key ranges that
-  // share an XCD's L2 narrowest (least HBM fetch at equal time).  At least
-  // one tile per split.
-  const int64_t target_wg = nqb >= 128 ? 4096 : (nqb >= 32 ? 1024 : 512);
-  int64_t per_cg = (target_wg + 8 * nqb_g - 1) / (8 * nqb_g);
+  int64_t per_cg = (sp + cgroups - 1) / cgroups;
   int64_t max_per_cg = S / (static_cast<int64_t>(cgroups) * kTileCols);
   if (max_per_cg < 1) max_per_cg = 1;
   if (per_cg > max_per_cg) per_cg = max_per_cg;
-  if (per_cg < 1) per_cg = 1;
   const int64_t splits = cgroups * per_cg;
   int64_t cps = (S + splits - 1) / splits;
   cps = (cps + kTileCols - 1) / kTileCols * kTileCols;

@@ -130,6 +130,12 @@ def _score_case(T, S_tokens, q_pos0_back, heads, dim, seed):
     (203, 2811, 203, 64, 128),  # ragged rows and columns, masked tail
     (77, 1500, 300, 40, 64),    # two partly filled head tiles
     (16, 9000, 16, 33, 128),
+    # many query blocks, few key tiles: one XCD column group with two splits, then
+    # one split; longer key ranges: two and four column groups
+    (2048, 2600, 2048, 16, 64),
+    (4096, 5000, 4096, 8, 32),
+    (2048, 9000, 2048, 4, 32),
+    (1024, 16400, 1024, 4, 32),
 ])
 def test_scores_match_oracle_and_fold_equals_second_pass(T, S_tokens, back, heads, dim):
     c, st, S, q_pos0, q, w = _score_case(T, S_tokens, back, heads, dim, seed=T + S_tokens)
