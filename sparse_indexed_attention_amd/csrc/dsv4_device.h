@@ -79,15 +79,16 @@ __device__ __forceinline__ int64_t visible_rows(int64_t p, int ratio) {
 // (global_load_lds_dwordx4): lane L of the wave writes lds_wave_base + 16*L.
 // Issued as inline asm so the compiler neither reorders it nor adds its own
 // conservative vmcnt(0) waits for it; callers wait with s_waitcnt vmcnt before
-// the barrier that publishes the data.  Issued after the compiler's own loads,
+// the barrier that publishes the data.  The LDS address goes in m0 as an
+// operand, so the compiler sets m0 itself and knows it is in use.  Issued after the compiler's own loads,
 // these can only make the compiler's in-order vmcnt waits stricter.
 __device__ __forceinline__ void global_to_lds16(const void* g, const void* lds_wave_base) {
   const uint32_t lds = static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_wave_base));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("global_load_lds_dwordx4 %0, off"
                :
-               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "m0");
+               : "v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
 }
 
 // Same, addressed as a wave-uniform 64-bit base (SGPR pair) plus a 32-bit
@@ -96,10 +97,10 @@ __device__ __forceinline__ void global_to_lds16_s(const void* sbase, uint32_t vo
                                                   const void* lds_wave_base) {
   const uint32_t lds = static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_wave_base));
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("global_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "m0");
+               : "v"(voff), "s"(sbase), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
 }
 
 // s_waitcnt immediates (gfx9 encoding): vmcnt(n) with the other counters open,
