@@ -521,7 +521,7 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
               uint32_t c1 = 0u;
 #pragma unroll
               for (int e = 0; e < kCE; ++e) {
-                if (64u * e >= in_bin) break;  // uniform
+                if (64u * e >= in_bin) continue;  // uniform (a break would stop the unrolling)
                 const bool one = ((alive >> e) & 1u) && ((x[e] >> b) & 1u);
                 ones |= static_cast<uint32_t>(one) << e;
                 c1 += static_cast<uint32_t>(__popcll(__ballot(one)));
