@@ -138,7 +138,29 @@ def _score_case(T, S_tokens, q_pos0_back, heads, dim, seed):
     (1024, 16400, 1024, 4, 32),
 ])
 def test_scores_match_oracle_and_fold_equals_second_pass(T, S_tokens, back, heads, dim):
-    c, st, S, q_pos0, q, w = _score_case(T, S_tokens, back, heads, dim, seed=T + S_tokens)
+    _check_scores(T, S_tokens, back, heads, dim, seed=T + S_tokens)
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_scores_random_shapes_match_oracle(case):
+    """Seeded random shapes over every kernel variant (head counts 1-64 in one
+    or two 32-head tiles, dims 32/64/128), 1 to 2,048 query rows and up to
+    3,000 pooled rows, so that the launch takes one to eight XCD column groups,
+    one or many splits per group, and splits that start past the last key."""
+    rng = np.random.default_rng(5000 + case)
+    heads = int(rng.choice([1, 4, 16, 33, 40, 64]))
+    dim = int(rng.choice([32, 64, 128]))
+    while True:
+        T = int(np.exp(rng.uniform(0.0, np.log(2048.0))))  # log-uniform, 1 .. 2,047
+        S_tokens = int(rng.integers(max(T, 16), 12001))
+        if T * (S_tokens // 4) * heads * dim <= 2.5e9:  # oracle time
+            break
+    back = int(rng.integers(T, min(S_tokens, T + 3000) + 1))
+    _check_scores(T, S_tokens, back, heads, dim, seed=6000 + case)
+
+
+def _check_scores(T, S_tokens, back, heads, dim, seed):
+    c, st, S, q_pos0, q, w = _score_case(T, S_tokens, back, heads, dim, seed=seed)
     stride = dsv4.dsv4_score_stride(S)
     folded = torch.full((T, stride), 7.0, device="cuda")
     raw = torch.full((T, stride), 7.0, device="cuda")
