@@ -152,6 +152,11 @@ int dsv4_compress(dsv4_pool_cache* cache, const void* x, int64_t n_new, void* st
  * pooled-ratio causal mask folded into the score epilogue [P2 commit 5]);
  * fold_mask = 0: every s < S is scored (second-pass masking is then the
  * caller's, with the same -inf sentinel).
+ * Each entry is computed by one workgroup in a fixed order (fp32 products
+ * of the bf16 inputs summed over dim in MFMA order, then over heads), so an
+ * unmasked entry's bits depend only on q[t], w[t] and key[s]: not on rows,
+ * nor on how the launch splits the rows and columns.  A row's scores are the
+ * same in any tile and run to run.
  * Shape gate: bf16 ratio-4 cache, dim in {32, 64, 128}, 1 <= n_heads <= 64,
  * S <= out_stride <= 2^28 - 64 (UNSUPPORTED beyond).
  */

@@ -159,6 +159,28 @@ def test_scores_random_shapes_match_oracle(case):
     _check_scores(T, S_tokens, back, heads, dim, seed=6000 + case)
 
 
+def test_scores_bitwise_independent_of_launch_shape():
+    """A row's scores are the same bits whichever call computes them: a 2,048-row
+    launch (few long splits), sub-ranges of 1, 64, 1,000 and 48 rows (more, shorter
+    splits and other XCD column groups) and the rows one call at a time for a few."""
+    T, S_tokens, heads, dim = 2048, 36000, 64, 128
+    c, st, S, q_pos0, q, w = _score_case(T, S_tokens, T, heads, dim, seed=424242)
+    stride = dsv4.dsv4_score_stride(S)
+    qd, wd = bf16_t(q).cuda(), torch.from_numpy(w).cuda()
+    full = torch.empty((T, stride), device="cuda")
+    dsv4.dsv4_indexer_scores(c, qd, wd, q_pos0, full)
+    ranges = [(0, 1), (0, 64), (100, 1100), (2000, 2048), (777, 778), (1999, 2000)]
+    parts = []
+    for a, b in ranges:
+        out = torch.empty((b - a, stride), device="cuda")
+        dsv4.dsv4_indexer_scores(c, qd[a:b].contiguous(), wd[a:b].contiguous(), q_pos0 + a, out)
+        parts.append(out)
+    torch.cuda.synchronize()
+    f = full[:, :S].cpu().numpy().view(np.uint32)
+    for (a, b), out in zip(ranges, parts):
+        assert np.array_equal(out[:, :S].cpu().numpy().view(np.uint32), f[a:b]), (a, b)
+
+
 def _check_scores(T, S_tokens, back, heads, dim, seed):
     c, st, S, q_pos0, q, w = _score_case(T, S_tokens, back, heads, dim, seed=seed)
     stride = dsv4.dsv4_score_stride(S)
