@@ -1,5 +1,6 @@
 """Top-k of rows held in registers (at most 32,768 visible columns: one wave
-per row up to 4,096 columns, else 2, 4 or 8 waves of 4,096 columns each):
+per row up to 4,096 columns, else 2, 4 or 8 waves of 4,096 columns each; at
+most 1,024 rows of 2,049 - 4,096 columns take 2 waves of 2,048):
 parity with the oracle's selection and with the LDS-staged workgroup
 kernel, which the same entry point takes when the row stride is not a
 multiple of 4 floats or rows are longer.
@@ -71,7 +72,7 @@ def _select(scores, q_pos0, n_cols, topk, stride):
                                   "constant", "signed_zero", "wide"])
 def test_short_rows_match_oracle(max_vis, kind):
     rng = np.random.default_rng(zlib.crc32(f"{kind}/{max_vis}".encode()))
-    rows = 70                                 # one wave per row: 18 workgroups, the last partial
+    rows = 70  # one wave per row (18 workgroups, the last partial) up to 2,048 columns
     q_pos0 = 4 * max_vis - rows               # the last row sees exactly max_vis columns
     n_cols = max_vis
     topk = 512 if max_vis <= 2049 else 2048
@@ -79,6 +80,20 @@ def test_short_rows_match_oracle(max_vis, kind):
     got, buf = _select(s, q_pos0, n_cols, topk, stride=n_cols + (-n_cols) % 4)
     want = O.topk_select(buf.astype(np.float64), q_pos0, topk)
     np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("max_vis", [2049, 3000, 4096])
+@pytest.mark.parametrize("kind", ["relu_sum", "levels3", "constant", "wide"])
+def test_many_rows_of_2k_to_4k_columns_one_wave_each(max_vis, kind):
+    """Past 1,024 rows, rows of 2,049 - 4,096 columns take one wave each (at most
+    1,024 take two waves of 2,048, covered above with 70 rows)."""
+    rng = np.random.default_rng(zlib.crc32(f"many/{kind}/{max_vis}".encode()))
+    rows = 1100
+    q_pos0 = 4 * max_vis - rows
+    n_cols = max_vis
+    s = _rows(kind, rows, n_cols, rng)
+    got, buf = _select(s, q_pos0, n_cols, 2048, stride=n_cols + (-n_cols) % 4)
+    np.testing.assert_array_equal(got, O.topk_select(buf.astype(np.float64), q_pos0, 2048))
 
 
 @pytest.mark.parametrize("topk", [1, 2, 63, 64, 65, 1000, 1023, 1024, 4096])
