@@ -649,8 +649,8 @@ topk_kernel(const float* __restrict__ scores, int64_t rows, int64_t stride, int6
 // Rows held in registers (at most 32,768 visible columns): one wave per row
 // up to 64 * KPL <= 4,096 columns (kShortWaves rows per workgroup, no
 // workgroup barriers), else NW = 2, 4 or 8 waves of 4,096 columns each; few
-// rows of 2,049 - 4,096 columns take 2 waves of 2,048.  The same selection
-// rule as above:
+// rows of 2,049 - 16,384 columns take 2, 4 or 8 waves of 2,048.  The same
+// selection rule as above:
 //   * lane L holds the float4 at columns 256v + 4L .. 256v + 4L + 3 of its
 //     wave's block for v = 0 .. KPL/4 - 1 (each load instruction reads 1 KiB
 //     contiguous), as keys key[4v + i]; columns past the visible prefix get
@@ -779,8 +779,8 @@ topk_reg_kernel(const RegArgs a) {
   const int topk = a.topk, cap = a.cap, words = a.words;
   int32_t* const __restrict__ out_idx = a.out_idx;
   static_assert(KPL % 4 == 0 && KPL <= 64, "keys per lane");
-  static_assert(NW == 1 || KPL == 64 || (NW == 2 && KPL == 32),
-                "rows of several waves hold 4,096 columns per wave, or 2 x 2,048");
+  static_assert(NW == 1 || KPL == 64 || KPL == 32,
+                "rows of several waves hold 4,096 or 2,048 columns per wave");
   constexpr int kSteps = KPL / 4;
   constexpr int kRowsPerWG = NW == 1 ? kShortWaves : 1;
   constexpr int kCols = 64 * KPL;  // columns of one wave
@@ -1177,13 +1177,15 @@ template <int PASS>
 hipError_t launch_reg(RegArgs a, int64_t max_cols, hipStream_t s) {
   const int64_t items = PASS == kRegChunk ? a.rows * a.cpr : a.rows;
   a.cap = static_cast<int>(max_cols < a.topk ? max_cols : a.topk);  // chosen slots per item
-  // Items of 2,049 - 4,096 columns take one wave each when there are many of
-  // them (2,048 rows fill the chip with single waves, and the row's waves'
-  // exchanges would only add work), two waves of 2,048 columns when there
-  // are at most 1,024 (a lone wave's row is latency-bound: one row at 16K
-  // context takes 8 us in two waves, 11 us in one).
-  const bool two_short = PASS != kRegChunk && max_cols > 32 * 64 && max_cols <= 64 * 64 &&
-                         items <= 1024;
+  // Few items of 2,049 - 16,384 columns take twice the waves, 2,048 columns
+  // each: a row on few waves is latency-bound (one row of 4,096 columns
+  // takes 8 us on two waves, 10 us on one; of 8,192, 8.5 us on four, 11.6
+  // us on two).  Many items fill the chip anyway, and the extra waves'
+  // exchanges only add work (at 1,024 rows of 16,384 columns eight waves
+  // each take 32 us, four 29 us).
+  const bool wide = PASS != kRegChunk && max_cols > 32 * 64 && max_cols <= 4 * 64 * 64 &&
+                    items <= (max_cols > 2 * 64 * 64 ? 512 : 1024);
+  const bool two_short = wide && max_cols <= 64 * 64;
   if (PASS != kRegChunk && max_cols <= 64 * 64 && !two_short) {
     // one wave per item, kShortWaves items per workgroup; per wave the
     // histogram, later the chosen columns + 64 spare slots (16-bit)
@@ -1211,9 +1213,13 @@ hipError_t launch_reg(RegArgs a, int64_t max_cols, hipStream_t s) {
   constexpr int P2 = PASS == kRegChunk ? kRegRows : PASS;  // chunk items take 8 waves
   if (PASS == kRegChunk || max_cols > 4 * 64 * 64)
     hipLaunchKernelGGL((topk_reg_kernel<64, 8, PASS>), grid, dim3(512), lds, s, a);
+  else if (max_cols > 2 * 64 * 64 && wide)
+    hipLaunchKernelGGL((topk_reg_kernel<32, 8, P2>), grid, dim3(512), lds, s, a);
   else if (max_cols > 2 * 64 * 64)
     hipLaunchKernelGGL((topk_reg_kernel<64, 4, P2>), grid, dim3(256), lds, s, a);
-  else if (!two_short)
+  else if (max_cols > 64 * 64 && wide)
+    hipLaunchKernelGGL((topk_reg_kernel<32, 4, P2>), grid, dim3(256), lds, s, a);
+  else if (max_cols > 64 * 64)
     hipLaunchKernelGGL((topk_reg_kernel<64, 2, P2>), grid, dim3(128), lds, s, a);
   else
     hipLaunchKernelGGL((topk_reg_kernel<32, 2, P2>), grid, dim3(128), lds, s, a);

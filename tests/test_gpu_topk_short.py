@@ -1,6 +1,6 @@
 """Top-k of rows held in registers (at most 32,768 visible columns: one wave
-per row up to 4,096 columns, else 2, 4 or 8 waves of 4,096 columns each; at
-most 1,024 rows of 2,049 - 4,096 columns take 2 waves of 2,048):
+per row up to 4,096 columns, else 2, 4 or 8 waves of 4,096 columns each; few
+rows of 2,049 - 16,384 columns take 2, 4 or 8 waves of 2,048):
 parity with the oracle's selection and with the LDS-staged workgroup
 kernel, which the same entry point takes when the row stride is not a
 multiple of 4 floats or rows are longer.
@@ -82,13 +82,13 @@ def test_short_rows_match_oracle(max_vis, kind):
     np.testing.assert_array_equal(got, want)
 
 
-@pytest.mark.parametrize("max_vis", [2049, 3000, 4096])
+@pytest.mark.parametrize("max_vis,rows", [(2049, 1100), (3000, 1100), (4096, 1100),
+                                          (4097, 1100), (8192, 1100), (8193, 600), (16384, 600)])
 @pytest.mark.parametrize("kind", ["relu_sum", "levels3", "constant", "wide"])
-def test_many_rows_of_2k_to_4k_columns_one_wave_each(max_vis, kind):
-    """Past 1,024 rows, rows of 2,049 - 4,096 columns take one wave each (at most
-    1,024 take two waves of 2,048, covered above with 70 rows)."""
+def test_many_rows_keep_4096_columns_per_wave(max_vis, rows, kind):
+    """Past 1,024 rows (512 beyond 8,192 columns) rows keep one wave per 4,096
+    columns; fewer rows take waves of 2,048, covered above with 70 rows."""
     rng = np.random.default_rng(zlib.crc32(f"many/{kind}/{max_vis}".encode()))
-    rows = 1100
     q_pos0 = 4 * max_vis - rows
     n_cols = max_vis
     s = _rows(kind, rows, n_cols, rng)
