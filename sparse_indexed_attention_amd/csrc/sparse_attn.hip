@@ -325,9 +325,10 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
   };
 
   // Software pipeline, one workgroup barrier per tile.  Iteration `tile`
-  // finishes that tile (its partner partial, softmax, P.V) while computing
-  // the next tile's partial S^T, so the MFMAs of QK(tile+1) run beside the
-  // softmax VALU work.  Stage use at iteration `tile`: tile (P.V), tile+1
+  // finishes that tile (its partner partial, softmax, P.V) and computes the
+  // next tile's partial S^T: half the head groups before their softmax, so
+  // the MFMAs of QK(tile+1) run beside its VALU work, the other half after
+  // their P.V.  Stage use at iteration `tile`: tile (P.V), tile+1
   // (QK), tile+2 (gather in flight, into the stage tile-1 released).
   // Validity masks of the tiles in flight: current, next, and the one after.
   // An empty split (fewer tiles than splits) skips the pipeline and leaves
@@ -368,8 +369,13 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
 
       f32x4_t sacc0 = s_own0, sacc1 = s_own1;
       add_partner(tile, sacc0, sacc1);
-      // the next tile's partial S^T: its MFMAs overlap the softmax below
-      if (tile + 1 < n_tiles) qk(tile + 1, s_own0, s_own1);
+      // The next tile's partial S^T.  Head groups 0-1 compute it here, so its
+      // MFMAs overlap their softmax; the other half after their P.V, so the
+      // eight waves' fragment reads of tile+1 do not all follow the barrier
+      // at once (same results either way: the partials are published by the
+      // next iteration's barrier).
+      const bool qk_first = hg < (NHG + 1) / 2;
+      if (qk_first && tile + 1 < n_tiles) qk(tile + 1, s_own0, s_own1);
 
       // lane holds, for head l16, keys mt*16 + 4*i + kb (output rows 4*kb + i)
       float sv[8];
@@ -405,7 +411,7 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
         pk[3] = pack_bf16x2(pr[6], pr[7]);
         pa = *reinterpret_cast<const bf16x8_t*>(pk);
       }
-      if (tile + 1 < n_tiles) put_partial(tile + 1, s_own0, s_own1);
+      if (qk_first && tile + 1 < n_tiles) put_partial(tile + 1, s_own0, s_own1);
       if (__ballot(bump)) {
         const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
         l_run *= alpha;
@@ -420,6 +426,10 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
       m_ref = m_new;
       l_run += psum;
       pv(tile, pa);
+      if (!qk_first && tile + 1 < n_tiles) {
+        qk(tile + 1, s_own0, s_own1);
+        put_partial(tile + 1, s_own0, s_own1);
+      }
     }
   }
   if (nsplit > 1) {
