@@ -121,7 +121,15 @@ sparse_attn_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, int H, float 
   const int kb = lane >> 4;    // 16-lane group
   const int l16 = lane & 15;
 
-  const int64_t t = blockIdx.x;
+  // XCD-contiguous queries: workgroup b runs on XCD b % 8, which takes the
+  // (b % 8)-th eighth of the queries, so neighbours (whose selections and
+  // windows overlap) share that XCD's L2.  A bijection for any gridDim.x.
+  int64_t t;
+  {
+    const int64_t nq = gridDim.x, full = nq / 8, rem = nq % 8;
+    const int64_t x = blockIdx.x % 8, r = blockIdx.x / 8;
+    t = x * full + (x < rem ? x : rem) + r;
+  }
   const int split = blockIdx.y;  // key split (nsplit > 1: partial results)
   const int64_t p = q_pos0 + t;
   const int64_t lo = (p - window + 1) > 0 ? (p - window + 1) : 0;
