@@ -547,3 +547,63 @@ def test_compressed_attention_ratio128_matches_masked_sdpa():
             mask[t, raw.shape[0] + s_] = 128 * s_ + 127 <= p
     assert mask[:, raw.shape[0]:].sum(axis=1).tolist() == [2, 2, 3, 3, 3, 3]
     np.testing.assert_allclose(got, _masked_sdpa(q, keys, mask, 0.3), rtol=1e-10, atol=1e-12)
+
+
+def test_attention_repeated_slot_counts_once_per_listing():
+    # Reading: a pooled row listed in two selection slots is two keys (each
+    # slot is one key of the softmax).  SDPA over the key list [raw rows ;
+    # pooled rows ; one more copy of every repeated row] with each copy
+    # unmasked fixes that independently of the oracle's own loop.
+    rng = np.random.default_rng(21)
+    T, H, D, W, q_pos0 = 4, 3, 8, 3, 40
+    raw_pos0 = q_pos0 - W + 1
+    raw = rng.standard_normal((T + W - 1, D))
+    S = (q_pos0 + T) // 4
+    pooled = rng.standard_normal((S, D))
+    q = rng.standard_normal((T, H, D))
+    sel = np.full((T, 5), -1, dtype=np.int32)
+    sel[0, :4] = [2, 7, 7, 9]          # row 7 twice
+    sel[1, :5] = [5, 1, 5, 5, 3]       # row 5 three times, unsorted
+    sel[2, :3] = [0, 0, 9]
+    sel[3, :2] = [4, 8]                # no repeat
+    scale = 0.4
+    got = O.sparse_prefill_attention(q, q_pos0, raw, raw_pos0, W, pooled, sel, scale)
+    extra = [(t, int(s)) for t in range(T) for j, s in enumerate(sel[t])
+             if s >= 0 and s in sel[t, :j]]
+    keys = np.concatenate([raw, pooled, np.stack([pooled[s] for _, s in extra])], axis=0)
+    mask = np.zeros((T, keys.shape[0]), dtype=bool)
+    for t in range(T):
+        p = q_pos0 + t
+        for j in range(raw.shape[0]):
+            mask[t, j] = p - W < raw_pos0 + j <= p
+        for s in set(int(s) for s in sel[t] if s >= 0):
+            assert s < O.visible_rows(p)
+            mask[t, raw.shape[0] + s] = True
+    for e, (t, _) in enumerate(extra):
+        mask[t, raw.shape[0] + S + e] = True
+    assert len(extra) == 4
+    np.testing.assert_allclose(got, _masked_sdpa(q, keys, mask, scale), rtol=1e-10, atol=1e-12)
+    # and it differs from attending each distinct row once
+    once = sel.copy()
+    once[0, 2] = once[1, 2] = once[1, 3] = once[2, 1] = -1
+    assert np.abs(O.sparse_prefill_attention(q, q_pos0, raw, raw_pos0, W, pooled, once, scale)
+                  - got)[:3].max() > 1e-3
+
+
+def test_tile_matrix_golden_scratch_sizes():
+    # [P3 Summary; Suggested acceptance and benchmark matrix]: the score
+    # scratch at 1M context is tile rows x pooled rows x 4 B.  The page
+    # estimates about 4 GiB untiled at chunk 4,096 (262,146 rows); the
+    # matrix lists the (global chunk, indexer tile) pairs to measure.
+    g = golden("p3_tile_matrix.json")
+    rows = g["compressed_rows_at_1M_context_approx"]
+    untiled = 4096 * rows * 4
+    assert round(untiled / 2 ** 30) == g["indexer_scores_bytes_at_chunk_4096_approx_GiB"]
+    for chunk, tile in g["matrix"]:
+        assert tile <= chunk and chunk % tile == 0
+        # one reused scratch: the tile, not the chunk, sets its size
+        assert tile * rows * 4 <= untiled
+    assert [4096, 1024] in g["matrix"] and [1024, 1024] in g["matrix"]
+    # the bench's (chunk, tile) matrix is the page's list
+    import bench
+    assert [list(m) for m in bench.MATRIX] == g["matrix"]
