@@ -95,7 +95,12 @@ typedef struct dsv4_pool_cache {
   int32_t dtype;
 } dsv4_pool_cache;
 
-/* Capability probe: returns DSV4_ABI_VERSION of the loaded library. */
+/*
+ * Capability probe [P2 commit 5: callers probe the kernel's signature once
+ * and fall back when the fused form is absent]: returns DSV4_ABI_VERSION of
+ * the loaded library, so a caller built against a newer header can detect
+ * an older library before calling entry points it lacks.
+ */
 int dsv4_abi_version(void);
 
 /* Message describing the last failed call on this thread ("" if none). */
@@ -250,6 +255,8 @@ int dsv4_indexer_select(const dsv4_pool_cache* index_cache, int64_t n_attn_rows,
  *           with the indexer's sel_idx (or NULL on the small-pool path).
  * sel_idx : device int32 [T][topk] or NULL.
  * out     : device bf16 [T][n_heads][head_dim].
+ * q, raw_kv, out and the cache rows must be 16-byte aligned (the kernel
+ * moves them in 16-byte vectors); INVALID_ARG otherwise.
  * scale <= 0 selects 1/sqrt(head_dim).
  * Shape gate: head_dim in {32, 64, 128, 256, 512}, 1 <= n_heads <= 64,
  * window >= 1, topk <= DSV4_MAX_TOPK.

@@ -357,9 +357,10 @@ static int check_attn_args(const char* who, const void* q, int64_t T, int64_t q_
     return DSV4_OK;
   }
   if (!q || !raw_kv || !out) return fail(DSV4_ERR_INVALID_ARG, "%s: NULL buffer", who);
-  if (!aligned16(q) || !aligned16(raw_kv) || (attn_cache && !aligned16(attn_cache->rows)))
-    return fail(DSV4_ERR_INVALID_ARG, "%s: q, raw_kv and cache rows must be 16-byte aligned",
-                who);
+  if (!aligned16(q) || !aligned16(raw_kv) || !aligned16(out) ||
+      (attn_cache && !aligned16(attn_cache->rows)))
+    return fail(DSV4_ERR_INVALID_ARG,
+                "%s: q, raw_kv, out and cache rows must be 16-byte aligned", who);
   const int64_t need_lo = (q_pos0 - window + 1) > 0 ? (q_pos0 - window + 1) : 0;
   if (raw_pos0 > need_lo || raw_pos0 + n_raw < q_pos0 + T)
     return fail(DSV4_ERR_INVALID_ARG,

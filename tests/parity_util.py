@@ -125,3 +125,137 @@ def assert_selection_matches(gpu_idx, ref_scores, q_pos0, topk):
             assert abs(r[s] - rk) <= band, f"row {t}: index {s} far from the threshold"
         n_band_rows += 1
     return n_band_rows
+
+
+# ---------------------------------------------------------------- row samples
+
+def spread_rows(T: int, n: int, tile: int = 0, seed: int = 0, shares: int = 8):
+    """About ``n`` rows of a T-row chunk, spread over ``shares`` equal
+    contiguous shares (the attention kernel deals queries to the eight XCDs
+    in contiguous eighths, so every share is a different XCD's work): each
+    share's first and last row and seeded random rows inside it, plus the
+    first and last row of every ``tile``-row query tile and both rows around
+    every share's middle 4-token boundary."""
+    rows = set()
+    rng = np.random.default_rng(seed)
+    bounds = [T * i // shares for i in range(shares + 1)]
+    per = max(2, n // shares)
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        if b <= a:
+            continue
+        rows.update({a, b - 1})
+        m = (a + b) // 2 // 4 * 4
+        rows.update({m - 1, m})
+        rows.update(int(r) for r in rng.integers(a, b, size=max(0, per - 4)))
+    if tile:
+        for t0 in range(0, T, tile):
+            rows.update({t0, min(T, t0 + tile) - 1})
+    return sorted(r for r in rows if 0 <= r < T)
+
+
+# ---------------------------------------------------------------- needle attention
+# With N(0,1) queries over ~2,000 keys the softmax is nearly flat, and leaving
+# out a whole 32-key group of keys moves the output by less than the 2e-2 bar.
+# Needle queries make every 32-key group decisive: each query's key list
+# (window rows oldest first, then the selection's slots in order -- the order
+# the attention walks its keys) is cut into groups of 32, one key of each
+# group is a needle for one head (groups dealt to heads round-robin), and that
+# head's query is a sum of its needles scaled so that each needle's logit is
+# about ln(number of keys): each needle then carries a large share of its
+# head's softmax.  A pooled needle is first projected off the span of the
+# query's window rows, so the window keys (larger than pooled rows) get no
+# large logits from it.  A skipped, repeated or wrongly gathered group moves
+# its head's output far beyond that head's bar (``check_needle_rows``).
+
+NEEDLE_GROUP = 32
+
+
+def attention_keys(t, q_pos0, window, raw, raw_pos0, pooled, sel, ratio=4):
+    """(key rows of query t in walk order, float64 [n, D]; window key count)."""
+    p = q_pos0 + t
+    lo = max(0, p - window + 1)
+    keys = [np.asarray(raw[j - raw_pos0], dtype=np.float64) for j in range(lo, p + 1)]
+    n_win = len(keys)
+    if pooled is not None:
+        vis = O.visible_rows(p, ratio)
+        slots = range(vis) if sel is None else [int(s) for s in sel[t] if 0 <= int(s) < vis]
+        keys += [np.asarray(pooled[s], dtype=np.float64) for s in slots]
+    return np.stack(keys, axis=0), n_win
+
+
+def needle_queries(T, q_pos0, H, window, raw, raw_pos0, pooled, sel, scale, seed=0,
+                   ratio=4, noise=0.1, rows=None):
+    """bf16-exact attention queries [T, H, D] with one needle per 32-key group
+    (for the queries in ``rows``, default all; the others are plain noise).
+
+    ``sel`` rows must hold their valid slots first (trailing -1 only), so the
+    slot order equals the key order."""
+    rng = np.random.default_rng(seed)
+    D = np.asarray(raw).shape[1]
+    q = rng.standard_normal((T, H, D), dtype=np.float32) * np.float32(noise)
+    for t in (range(T) if rows is None else rows):
+        K, n_win = attention_keys(t, q_pos0, window, raw, raw_pos0, pooled, sel, ratio)
+        U = np.linalg.qr(K[:n_win].T)[0]                 # [D, n_win] orthonormal
+        n = K.shape[0]
+        target = np.log(n)
+        for g in range((n + NEEDLE_GROUP - 1) // NEEDLE_GROUP):
+            j = g * NEEDLE_GROUP + int(rng.integers(0, min(NEEDLE_GROUP, n - g * NEEDLE_GROUP)))
+            k = K[j]
+            d = k if j < n_win else k - U @ (U.T @ k)
+            q[t, g % H] += target / (scale * float(d @ k)) * d
+    return SI.as_bf16_values(q.astype(np.float32))
+
+
+def group_power(q_row, K, scale):
+    """Per head h: the smallest change of that head's output (max |.| over
+    dims) when one of the 32-key groups dealt to h (groups g with g % H == h)
+    is left out or counted twice; inf for a head with no group."""
+    q_row = np.asarray(q_row, dtype=np.float64)
+    H = q_row.shape[0]
+    logits = scale * (q_row @ K.T)                       # [H, n]
+    e = np.exp(logits - logits.max(axis=1, keepdims=True))
+    num = e @ K                                          # [H, D]
+    den = e.sum(axis=1, keepdims=True)
+    out = num / den
+    power = np.full(H, np.inf)
+    n = K.shape[0]
+    for g, g0 in enumerate(range(0, n, NEEDLE_GROUP)):
+        h = g % H
+        eg = e[h, g0:g0 + NEEDLE_GROUP]
+        ng = eg @ K[g0:g0 + NEEDLE_GROUP]
+        dg = eg.sum()
+        dup = np.abs((num[h] + ng) / (den[h, 0] + dg) - out[h]).max()
+        drop = np.abs((num[h] - ng) / (den[h, 0] - dg) - out[h]).max() if den[h, 0] > dg * (1 + 1e-12) else np.inf
+        power[h] = min(power[h], drop, dup)
+    return power
+
+
+def _bf16_ulp(x):
+    x = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(x)) - 7)
+
+
+def check_needle_rows(g_out, rows, q, q_pos0, window, raw, raw_pos0, pooled, sel, scale,
+                      ratio=4, atol=None):
+    """GPU output rows vs the fp64 oracle, head by head, at a bar of
+    min(2e-2, a quarter of the smallest change one of the head's groups
+    makes when left out or counted twice): a single skipped, repeated or
+    wrongly gathered 32-key group fails its head.  Each bar must stay at
+    least one bf16 ulp of the head's largest output (twice the rounding of
+    the bf16 output), so that output rounding alone cannot fail it (the
+    case's own power, checked on the oracle)."""
+    atol = ATTN_ATOL if atol is None else atol
+    worst = 0.0
+    for i, t in enumerate(rows):
+        ref = O.sparse_prefill_attention(q[t:t + 1], q_pos0 + t, raw, raw_pos0, window, pooled,
+                                         None if sel is None else sel[t:t + 1], scale,
+                                         ratio=ratio)[0]
+        K, _ = attention_keys(t, q_pos0, window, raw, raw_pos0, pooled, sel, ratio)
+        bar = np.minimum(atol, group_power(q[t], K, scale) / 4)   # [H]
+        floor = _bf16_ulp(np.abs(ref).max(axis=1))
+        assert np.all(bar >= floor), (t, np.argmin(bar - floor), bar.min())
+        err = np.abs(np.asarray(g_out[i], dtype=np.float64) - ref).max(axis=1)   # [H]
+        bad = np.nonzero(err > bar)[0]
+        assert bad.size == 0, (t, [(int(h), float(err[h]), float(bar[h])) for h in bad[:4]])
+        worst = max(worst, float(err.max()))
+    return worst

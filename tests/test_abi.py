@@ -116,11 +116,14 @@ def test_attention_gates():
     c = _cache(n_rows=40, dim=512, cap=64)
 
     def call(T=4, q_pos0=100, heads=64, dim=512, raw_pos0=0, n_raw=104, window=128, cache=c,
-             sel=FAKE, topk=16):
+             sel=FAKE, topk=16, out=FAKE):
         return _rc("dsv4_sparse_prefill_attn", ctypes.c_void_p(FAKE), T, q_pos0, heads, dim, 0.0,
                    ctypes.c_void_p(FAKE), raw_pos0, n_raw, window, ctypes.byref(cache),
-                   ctypes.c_void_p(sel), topk, ctypes.c_void_p(FAKE), None)
+                   ctypes.c_void_p(sel), topk, ctypes.c_void_p(out), None)
     assert call(dim=96) == UNSUPPORTED
+    # the output is written in 16-byte vectors: an offset view is refused
+    assert call(out=FAKE + 8) == INVALID
+    assert "aligned" in dsv4.dsv4_last_error()
     assert call(dim=256) == INVALID           # cache dim differs
     assert call(heads=65) == UNSUPPORTED
     assert call(window=0) == INVALID
@@ -166,6 +169,9 @@ def test_narrow_attention_plan_and_gates():
     assert call(n_splits=65) == UNSUPPORTED
     assert call(ws=0) == INVALID
     assert call(ws=FAKE + 4) == INVALID                       # not 16-byte aligned
+    assert _rc("dsv4_sparse_attn_narrow", ctypes.c_void_p(FAKE), 4, 100, 64, 512, 0.0,
+               ctypes.c_void_p(FAKE), 0, 104, 128, ctypes.byref(c), ctypes.c_void_p(FAKE), 16,
+               4, ctypes.c_void_p(FAKE), 1 << 30, ctypes.c_void_p(FAKE + 2), None) == INVALID
     assert call(nbytes=4 * 4 * 64 * 514 * 4 - 1) == SCRATCH   # one byte short
     assert "workspace" in dsv4.dsv4_last_error()
     assert call(T=0, n_splits=4, ws=0) == OK                  # nothing to do
