@@ -163,7 +163,8 @@ def spread_rows(T: int, n: int, tile: int = 0, seed: int = 0, shares: int = 8):
 # head's query is a sum of its needles scaled so that each needle's logit is
 # about ln(number of keys): each needle then carries a large share of its
 # head's softmax.  A pooled needle is first projected off the span of the
-# query's window rows, so the window keys (larger than pooled rows) get no
+# query's window rows (unless it lies mostly inside it: a pooled row of the
+# window's own tokens), so the window keys (larger than pooled rows) get no
 # large logits from it.  A skipped, repeated or wrongly gathered group moves
 # its head's output far beyond that head's bar (``check_needle_rows``).
 
@@ -189,21 +190,44 @@ def needle_queries(T, q_pos0, H, window, raw, raw_pos0, pooled, sel, scale, seed
     (for the queries in ``rows``, default all; the others are plain noise).
 
     ``sel`` rows must hold their valid slots first (trailing -1 only), so the
-    slot order equals the key order."""
+    slot order equals the key order.  A pooled row whose tokens all lie in
+    the query's window is a mean of window keys: it can never outweigh them,
+    and leaving it out barely moves the output, so a needle is drawn among
+    the other keys of its group (``without_window_rows`` removes such rows
+    from a selection)."""
     rng = np.random.default_rng(seed)
     D = np.asarray(raw).shape[1]
     q = rng.standard_normal((T, H, D), dtype=np.float32) * np.float32(noise)
     for t in (range(T) if rows is None else rows):
         K, n_win = attention_keys(t, q_pos0, window, raw, raw_pos0, pooled, sel, ratio)
         U = np.linalg.qr(K[:n_win].T)[0]                 # [D, n_win] orthonormal
+        perp = K[n_win:] - (K[n_win:] @ U) @ U.T          # pooled keys off the window span
+        ok = np.ones(K.shape[0], dtype=bool)
+        ok[n_win:] = np.einsum("ij,ij->i", perp, perp) >= 0.25 * np.einsum("ij,ij->i", K[n_win:], K[n_win:])
         n = K.shape[0]
         target = np.log(n)
         for g in range((n + NEEDLE_GROUP - 1) // NEEDLE_GROUP):
-            j = g * NEEDLE_GROUP + int(rng.integers(0, min(NEEDLE_GROUP, n - g * NEEDLE_GROUP)))
+            g0, g1 = g * NEEDLE_GROUP, min(n, (g + 1) * NEEDLE_GROUP)
+            cand = np.nonzero(ok[g0:g1])[0]
+            j = g0 + int(rng.choice(cand) if cand.size else rng.integers(0, g1 - g0))
             k = K[j]
-            d = k if j < n_win else k - U @ (U.T @ k)
+            d = k if (j < n_win or not ok[j]) else perp[j - n_win]
             q[t, g % H] += target / (scale * float(d @ k)) * d
     return SI.as_bf16_values(q.astype(np.float32))
+
+
+def without_window_rows(sel, q_pos0, window, ratio=4):
+    """Selection with the pooled rows whose tokens all lie inside the query's
+    window removed (valid slots compacted to the front, -1 after)."""
+    sel = np.asarray(sel)
+    out = np.full_like(sel, -1)
+    for t in range(sel.shape[0]):
+        p = q_pos0 + t
+        lo = max(0, p - window + 1)
+        vis = O.visible_rows(p, ratio)
+        keep = [int(s) for s in sel[t] if 0 <= int(s) < vis and ratio * int(s) < lo]
+        out[t, :len(keep)] = keep
+    return out
 
 
 def group_power(q_row, K, scale):

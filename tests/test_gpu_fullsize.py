@@ -9,10 +9,11 @@ Rows checked against the oracle:
 Pooled rows of the chunk and the all-pooled selections are checked in full.
 
 Attention is checked twice per workload: with the workload's N(0,1) queries
-(max |err| <= 2e-2 against fp64), and with needle queries built on the GPU's
-own selection, under which every 32-key group of keys carries a large share
-of one head's softmax, so that one skipped, repeated or wrongly gathered
-group fails (``parity_util.check_needle_rows``).
+on the GPU's own selection (max |err| <= 2e-2 against fp64), and with needle
+queries on that selection less its pooled rows made only of window tokens,
+under which every 32-key group of keys carries a large share of one head's
+softmax, so that one skipped, repeated or wrongly gathered group fails
+(``parity_util.check_needle_rows``).
 """
 import math
 
@@ -25,7 +26,8 @@ import synthetic_inputs as SI
 from oracle import dsv4_oracle as O
 
 from parity_util import (ATTN_ATOL, ChunkState, assert_scores_close, assert_selection_matches,
-                         bf16_t, check_needle_rows, needle_queries, spread_rows)
+                         bf16_t, check_needle_rows, needle_queries, spread_rows,
+                         without_window_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -124,13 +126,16 @@ def check_chunk(cs: ChunkState, tile: int, rows, attn_rows, needle_rows):
     g = out[attn_rows].float().cpu().numpy()
     check_random_q_attention(g, attn_rows, cs.inp["q_attn"], cs.q_pos0, cs.inp["raw_kv"],
                              cs.raw_pos0, W, pooled, gidx, D)
-    # needle queries on the same selection: every 32-key group decisive
+    # needle queries on the same selection (less the pooled rows made of
+    # window tokens): every 32-key group decisive
     scale = 1 / math.sqrt(D)
-    qn = needle_queries(T, cs.q_pos0, H, W, cs.inp["raw_kv"], cs.raw_pos0, pooled, gidx, scale,
+    nsel = without_window_rows(gidx, cs.q_pos0, W)
+    qn = needle_queries(T, cs.q_pos0, H, W, cs.inp["raw_kv"], cs.raw_pos0, pooled, nsel, scale,
                         seed=1, rows=needle_rows)
-    g = attention(qn, cs.q_pos0, cs.raw_kv, cs.raw_pos0, W, cs.acache, idx, H, D)
+    g = attention(qn, cs.q_pos0, cs.raw_kv, cs.raw_pos0, W, cs.acache,
+                  torch.from_numpy(nsel).cuda(), H, D)
     check_needle_rows(g[needle_rows].float().cpu().numpy(), needle_rows, qn, cs.q_pos0, W,
-                      cs.inp["raw_kv"], cs.raw_pos0, pooled, gidx, scale)
+                      cs.inp["raw_kv"], cs.raw_pos0, pooled, nsel, scale)
 
 
 def test_ctx4k_chunk2048_every_row():
@@ -210,11 +215,12 @@ def test_ctx16k_eight_chunks_skip_then_full():
         check_random_q_attention(g[arows].float().cpu().numpy(), arows, qa, q_pos0, raw_np,
                                  raw_pos0, W, pooled, gidx, D)
         nrows = spread_rows(T, 128, seed=100 + c)
-        qn = needle_queries(T, q_pos0, H, W, raw_np, raw_pos0, pooled, gidx, scale, seed=c,
+        nsel = without_window_rows(gidx, q_pos0, W)
+        qn = needle_queries(T, q_pos0, H, W, raw_np, raw_pos0, pooled, nsel, scale, seed=c,
                             rows=nrows)
-        g = attention(qn, q_pos0, raw_t, raw_pos0, W, acache, idx, H, D)
+        g = attention(qn, q_pos0, raw_t, raw_pos0, W, acache, torch.from_numpy(nsel).cuda(), H, D)
         check_needle_rows(g[nrows].float().cpu().numpy(), nrows, qn, q_pos0, W, raw_np,
-                          raw_pos0, pooled, gidx, scale)
+                          raw_pos0, pooled, nsel, scale)
     np.testing.assert_array_equal(icache.rows[:icache.n_rows].float().cpu().numpy(),
                                   ost.rows[:ost.n_rows])
     np.testing.assert_array_equal(acache.rows[:acache.n_rows].float().cpu().numpy(),
@@ -231,8 +237,9 @@ def test_ctx128k_needles_at_topk_4096():
     scale = 1 / math.sqrt(D)
     rng = np.random.default_rng(4096)
     sel = np.empty((T, k), np.int32)
-    for t in range(T):
-        sel[t] = np.sort(rng.choice(O.visible_rows(cs.q_pos0 + t), size=k, replace=False))
+    for t in range(T):   # rows older than the window (see without_window_rows)
+        old = (cs.q_pos0 + t - W + 1 + 3) // 4
+        sel[t] = np.sort(rng.choice(old, size=k, replace=False))
     rows = spread_rows(T, 64, seed=40)
     pooled = cs.oracle_pooled()
     qn = needle_queries(T, cs.q_pos0, H, W, cs.inp["raw_kv"], cs.raw_pos0, pooled, sel, scale,
@@ -346,9 +353,10 @@ def test_narrow_steps_at_end_of_context(wl, T):
                                        cs.oracle_pooled(), gidx, scale)
     err = np.abs(out.float().cpu().numpy() - ref_o).max()
     assert err <= ATTN_ATOL, err
-    qn = needle_queries(T, q0, H, W, raw_np, raw_lo, cs.oracle_pooled(), gidx, scale, seed=7)
+    nsel = without_window_rows(gidx, q0, W)
+    qn = needle_queries(T, q0, H, W, raw_np, raw_lo, cs.oracle_pooled(), nsel, scale, seed=7)
     dsv4.dsv4_sparse_attn_narrow(bf16_t(qn.reshape(T, H * D)).cuda().view(T, H, D), q0, raw,
-                                 raw_lo, W, cs.acache, idx, out, ns, ws)
+                                 raw_lo, W, cs.acache, torch.from_numpy(nsel).cuda(), out, ns, ws)
     torch.cuda.synchronize()
     check_needle_rows(out.float().cpu().numpy(), list(range(T)), qn, q0, W, raw_np, raw_lo,
-                      cs.oracle_pooled(), gidx, scale)
+                      cs.oracle_pooled(), nsel, scale)
