@@ -44,8 +44,9 @@ extern "C" {
 #endif
 
 /* 4: dsv4_indexer_select may keep top-k candidates in its scratch (the
- * scores are not left there), and dsv4_topk_select_split takes more rows. */
-#define DSV4_ABI_VERSION 4
+ * scores are not left there), and dsv4_topk_select_split takes more rows.
+ * 5: dsv4_indexer_select_noalloc. */
+#define DSV4_ABI_VERSION 5
 
 /* Return codes. */
 #define DSV4_OK                0
@@ -69,6 +70,8 @@ extern "C" {
 #define DSV4_MAX_HEADS       64
 #define DSV4_MAX_RATIO       256
 #define DSV4_MAX_ATTN_SPLITS 64
+/* Bytes of the per-GPU static score scratch of dsv4_indexer_select_noalloc. */
+#define DSV4_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
 
 /*
  * PoolingCache of one compressor [P1 Summary, Correctness; P2 commit 4].
@@ -234,6 +237,32 @@ int dsv4_indexer_select(const dsv4_pool_cache* index_cache, int64_t n_attn_rows,
                         int32_t n_heads, int32_t topk, int32_t tile_rows,
                         float* scratch, size_t scratch_bytes,
                         int32_t* out_idx, int32_t* out_all_pooled, void* stream);
+
+/*
+ * dsv4_indexer_select for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, checks, paths and output as
+ * dsv4_indexer_select (bit for bit), without the scratch: the score scratch
+ * is a static device array of DSV4_NOALLOC_SCRATCH_BYTES (32 MiB) that each
+ * GPU the library runs on holds until the process ends.  The call allocates
+ * and frees nothing; on a device's first call it looks the array's address
+ * up (hipGetSymbolAddress, with the current device = the stream's device).
+ * tile_rows = 0 takes the largest query-row tile whose scores fit the array
+ * (32 MiB / (4 * dsv4_score_stride(S)) rows: 256 at 32,768 pooled rows, 32 at
+ * 262,144); a tile_rows > 0 whose tile does not fit is refused with
+ * DSV4_ERR_SCRATCH before anything is enqueued (also when one row does not
+ * fit: more than 8,388,608 pooled rows).  The all-pooled and empty paths
+ * need no scratch.
+ * Every call on one GPU shares that GPU's array and leaves its last contents
+ * there (nothing in it needs clearing: each tile's scores are written before
+ * they are read).  Calls that overlap on one GPU -- on different streams or
+ * threads, or a captured graph replayed beside another call -- race on it:
+ * order them on one stream.
+ */
+int dsv4_indexer_select_noalloc(const dsv4_pool_cache* index_cache, int64_t n_attn_rows,
+                                const void* q, const float* w, int64_t T, int64_t q_pos0,
+                                int32_t n_heads, int32_t topk, int32_t tile_rows,
+                                int32_t* out_idx, int32_t* out_all_pooled, void* stream);
 
 /*
  * Fused windowed + pooled prefill attention [P2 commit 1; P3 Possible design

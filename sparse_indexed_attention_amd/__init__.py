@@ -20,6 +20,7 @@ __all__ = [
     "dsv4_indexer_scratch_bytes", "dsv4_compress", "dsv4_indexer_scores", "dsv4_topk_select",
     "dsv4_indexer_select", "dsv4_sparse_prefill_attn", "dsv4_sparse_attn_narrow_plan",
     "dsv4_sparse_attn_narrow", "dsv4_topk_split_workspace_bytes", "dsv4_topk_select_split",
+    "dsv4_indexer_select_noalloc", "DSV4_NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,6 +29,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "dsv4.h")
 
 DSV4_BF16 = 1
 DSV4_F32 = 2
+DSV4_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 RATIO = 4
 
 c_i32, c_i64, c_vp, c_f32, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
@@ -68,6 +70,9 @@ _SIGNATURES = {
     "dsv4_sparse_attn_narrow": (c_i32, [c_vp, c_i64, c_i64, c_i32, c_i32, c_f32, c_vp, c_i64,
                                         c_i64, c_i32, ctypes.POINTER(dsv4_pool_cache), c_vp,
                                         c_i32, c_i32, c_vp, c_sz, c_vp, c_vp]),
+    "dsv4_indexer_select_noalloc": (c_i32, [ctypes.POINTER(dsv4_pool_cache), c_i64, c_vp, c_vp,
+                                            c_i64, c_i64, c_i32, c_i32, c_i32, c_vp,
+                                            ctypes.POINTER(c_i32), c_vp]),
 }
 
 _lib = None
@@ -242,6 +247,24 @@ def dsv4_indexer_select(index_cache: PoolCache, n_attn_rows: int, q, w, T: int, 
     _check(lib().dsv4_indexer_select(index_cache.ref(), n_attn_rows, _ptr(q), _ptr(w), T, q_pos0,
                                      n_heads, topk, tile_rows, _ptr(scratch), nbytes,
                                      _ptr(out_idx), ctypes.byref(ap), _stream(stream)))
+    return bool(ap.value)
+
+
+def dsv4_indexer_select_noalloc(index_cache: PoolCache, n_attn_rows: int, q, w, T: int,
+                                q_pos0: int, n_heads: int, topk: int, out_idx: torch.Tensor,
+                                tile_rows: int = 0, stream=None) -> bool:
+    """dsv4_indexer_select with the library's static per-GPU scratch (no
+    scratch argument, nothing allocated).  Returns True on the all-pooled
+    path."""
+    if q is not None:
+        _need(q, torch.bfloat16, "q", 3)
+    if w is not None:
+        _need(w, torch.float32, "w", 2)
+    _need(out_idx, torch.int32, "out_idx", 2)
+    ap = c_i32(0)
+    _check(lib().dsv4_indexer_select_noalloc(index_cache.ref(), n_attn_rows, _ptr(q), _ptr(w), T,
+                                             q_pos0, n_heads, topk, tile_rows, _ptr(out_idx),
+                                             ctypes.byref(ap), _stream(stream)))
     return bool(ap.value)
 
 

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdsv4.so")
 
-DEVICE_SOURCES = ["compress.hip", "indexer_score.hip", "topk.hip", "sparse_attn.hip"]
+DEVICE_SOURCES = ["compress.hip", "indexer_score.hip", "topk.hip", "sparse_attn.hip",
+                  "noalloc.hip"]
 HOST_SOURCES = ["dsv4_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}"]

@@ -40,6 +40,18 @@ int hip_status(hipError_t e, const char* what) {
   return fail(DSV4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+}  // namespace
+
+int dsv4_internal_fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+namespace {
+
 // Pool ratios accepted by the compressor and the attention: 4 (indexer and
 // sparse attention) and 128 (CompressedAttention) are the pages'; any ratio
 // in [2, DSV4_MAX_RATIO] follows the same definitions.  The indexer entry

@@ -110,6 +110,10 @@ __device__ __forceinline__ constexpr int wait_vmcnt(int n) { return 0x0F70 | (n 
 
 }  // namespace dsv4
 
+// Records a failure in the library's thread-local error string (read by
+// dsv4_last_error) and returns `code`.
+int dsv4_internal_fail(int code, const char* fmt, ...);
+
 // Launch wrappers (defined next to their kernels).  All return hipError_t of
 // the launch; argument checks happen before they are called.
 hipError_t dsv4_launch_compress(void* rows, void* rem, int64_t n_rows, int32_t n_rem,

@@ -23,7 +23,7 @@ def test_library_exports_every_header_function():
 
 
 def test_abi_version_and_host_helpers():
-    assert dsv4.dsv4_abi_version() == 4
+    assert dsv4.dsv4_abi_version() == 5
     assert dsv4.dsv4_indexer_all_pooled(0, 8) is False
     assert dsv4.dsv4_indexer_all_pooled(1, 8) is True
     assert dsv4.dsv4_indexer_all_pooled(8, 8) is True
