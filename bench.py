@@ -21,10 +21,11 @@ oracle on a bounded sample of the same workload's query rows.
 `roofline.traffic` (HBM bytes per score-kernel launch) comes from the
 rocprofv3 counter summary profiles/traffic_indexer_score_<workload>.md and is
 reported only while the score kernel's sources still hash to the value
-recorded there (otherwise null).  That summary is made by two counter runs of
-this script with --calibration-copy (FETCH_SIZE, then WRITE_SIZE) and
-`bench.py --summarize-pmc FETCH_DB WRITE_DB OUT_MD --workload NAME`; the
-calibration copy scales each counter to bytes.
+recorded there (otherwise null).  It is written, with the counter summary
+profiles/counters_<workload>.md, by `bench.py --summarize-counters OUT_MD DB..`
+from rocprofv3 --pmc runs of `bench.py --lean --calibration-copy` (one
+counter set per run); the calibration copy scales FETCH_SIZE / WRITE_SIZE to
+bytes.
 """
 from __future__ import annotations
 
@@ -83,58 +84,151 @@ def recorded_traffic(workload: str):
         return None
 
 
-def summarize_pmc(fetch_db: str, write_db: str, out_md: str, workload: str, cmds: str):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE of the score kernel, scaled to bytes
-    by what the same counters read for the 1 GiB calibration copy."""
+KERNEL_CLASSES = (("indexer_score", "indexer_score_kernel"), ("topk", "topk_reg_kernel"),
+                  ("attention", "sparse_attn_kernel"), ("compress", "compress_kernel"),
+                  ("copy", "copy_kernel"))
+
+
+def read_counter_db(db: str) -> dict:
+    """{class: {"duration_ns": [...], counter: [...per dispatch...]}} from one
+    rocprofv3 --pmc database: SQ / TCC counters summed over their instances
+    per dispatch, GRBM_GUI_ACTIVE the largest instance (the XCDs run in
+    parallel)."""
     import sqlite3
+    c = sqlite3.connect(db)
+    rows = c.execute("select name, dispatch_id, counter_name, counter_value, duration "
+                     "from pmc_events").fetchall()
+    per = {}
+    for name, disp, cname, val, dur in rows:
+        cls = next((k for k, pat in KERNEL_CLASSES if pat in name), None)
+        if cls is None:
+            continue
+        d = per.setdefault(cls, {}).setdefault(disp, {"duration_ns": dur})
+        if cname.startswith("GRBM"):
+            d[cname] = max(d.get(cname, 0.0), val)
+        else:
+            d[cname] = d.get(cname, 0.0) + val
+    out = {}
+    for cls, disps in per.items():
+        keys = set().union(*[set(v) for v in disps.values()])
+        out[cls] = {k: [v[k] for v in disps.values() if k in v] for k in keys}
+    return out
 
-    def per_dispatch(db, counter):
-        c = sqlite3.connect(db)
-        rows = c.execute(
-            "select name, dispatch_id, sum(counter_value) from pmc_events "
-            "where counter_name = ? group by name, dispatch_id", (counter,)).fetchall()
-        score = [v for n, _, v in rows if SCORE_KERNEL in n]
-        copy = [v for n, _, v in rows if "elementwise" in n.lower()]
-        return score, copy
 
-    fs, fc = per_dispatch(fetch_db, "FETCH_SIZE")
-    ws, wc = per_dispatch(write_db, "WRITE_SIZE")
-    if not (fs and ws and fc and wc):
-        raise SystemExit("summarize-pmc: score or copy dispatches missing from the databases")
-    # the copy's largest dispatches are the 1 GiB calibration copies
-    fc, wc = sorted(fc)[-3:], sorted(wc)[-3:]
-    k_fetch = np.mean(fc) * 1024.0 / COPY_BYTES   # counter KiB per byte actually moved
-    k_write = np.mean(wc) * 1024.0 / COPY_BYTES
-    fetch_b = np.mean(fs) * 1024.0 / k_fetch
-    write_b = np.mean(ws) * 1024.0 / k_write
+def summarize_counters(out_md: str, dbs: list, workload: str, cmds: str):
+    """Counter summary of the hot path's kernels from several rocprofv3 --pmc
+    runs of `bench.py --lean --calibration-copy` (one counter set per run):
+    MFMA utilisation and engine clock of the score and attention kernels,
+    counter-measured HBM bytes of the score, top-k and attention kernels
+    (FETCH_SIZE / WRITE_SIZE scaled by the same counters' reading for the
+    1 GiB probe copy), LDS bank conflicts, instruction mix and wait shares.
+    Also rewrites the score kernel's traffic file the bench line reads."""
+    merged = {}
+    for db in dbs:
+        for cls, vals in read_counter_db(db).items():
+            m = merged.setdefault(cls, {})
+            for k, v in vals.items():
+                if k == "duration_ns":
+                    m.setdefault(k, []).extend(v)
+                else:
+                    m[k] = v
+    mean = lambda cls, k: float(np.mean(merged[cls][k])) if cls in merged and k in merged[cls] else None
     wl = SI.WORKLOADS[workload]
-    T = wl.chunk
-    pairs = sum((p + 1) // 4 for p in range(wl.q_pos0, wl.q_pos0 + T))
-    S = (wl.q_pos0 + T) // 4
-    algo = S * wl.idx_dim * 2 + T * wl.idx_heads * (wl.idx_dim * 2 + 4) + T * S * 4
+    T, H, D, k = wl.chunk, wl.heads, wl.head_dim, wl.topk
+    tile = wl.tile_rows or T
+    S = wl.n_rows_after
+    pos = range(wl.q_pos0 + T - tile, wl.q_pos0 + T)
+    pairs = sum((p + 1) // 4 for p in pos)
+    keys_q = [min(wl.window, p + 1) + min(k, (p + 1) // 4) for p in range(wl.q_pos0, wl.q_pos0 + T)]
+    algo = {
+        "indexer_score": {"flop": pairs * 2 * wl.idx_heads * wl.idx_dim,
+                          "bytes": S * wl.idx_dim * 2 + tile * wl.idx_heads * (wl.idx_dim * 2 + 4)
+                          + tile * S * 4},
+        "topk": {"bytes": pairs * 4 + tile * k * 4},
+        "attention": {"flop": sum(4 * H * D * n for n in keys_q),
+                      "bytes": sum(2 * D * n for n in keys_q) + 2 * T * H * D * 2 + T * k * 4},
+    }
+    # counter units per byte moved, from the probe copy (reads and writes COPY_BYTES)
+    kf = mean("copy", "FETCH_SIZE") * 1024.0 / COPY_BYTES if mean("copy", "FETCH_SIZE") else None
+    kw = mean("copy", "WRITE_SIZE") * 1024.0 / COPY_BYTES if mean("copy", "WRITE_SIZE") else None
+    lines = [f"# Counters of the hot-path kernels, {workload}", "",
+             "rocprofv3 --pmc runs of `bench.py --lean --calibration-copy` (warmup 1, 3 steps; each",
+             "kernel also runs in its own timed loop), one counter set per run.  Per dispatch, SQ",
+             "and TCC counters are summed over their instances and GRBM_GUI_ACTIVE is the largest",
+             "instance; figures are means over the kernel's dispatches.  Durations are those of the",
+             "counter runs (dispatches are serialised under counters).", "",
+             "Commands:", "", "```", cmds.strip(), "```", "",
+             f"- workload: `{workload}` ({T} query rows, tile {tile}, {S} pooled rows, k {k})",
+             f"- score_source_hash: `{score_source_hash()}`"]
+    if kf and kw:
+        lines += [f"- copy calibration: FETCH_SIZE {kf:.4f} KiB-units per byte read, "
+                  f"WRITE_SIZE {kw:.4f} per byte written (1 GiB probe copy, "
+                  f"{len(merged['copy']['FETCH_SIZE'])} dispatches)"]
+    lines += ["", "| kernel | dispatches | us (counters) | clock GHz | MFMA busy % | bf16 MFMA FLOP / algorithmic "
+              "| HBM read MB | HBM write MB | HBM total / algorithmic | LDS bank conflict % "
+              "| VALU / MFMA / LDS / SALU instr per wave | wait any % / dependency % |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    res = {}
+    for cls in ("indexer_score", "topk", "attention", "compress", "copy"):
+        if cls not in merged:
+            continue
+        dur = mean(cls, "duration_ns")
+        grbm = mean(cls, "GRBM_GUI_ACTIVE")
+        # (too short a dispatch gives no usable clock: the counter window
+        # is wider than the kernel)
+        clock = grbm / dur if grbm and dur and dur > 50e3 else None
+        busy = mean(cls, "SQ_VALU_MFMA_BUSY_CYCLES")
+        util = 100.0 * busy / (grbm * 1024) if busy is not None and grbm else None
+        mops = mean(cls, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        fl = algo.get(cls, {}).get("flop")
+        fl_ratio = (mops * 512 / fl) if mops is not None and fl else None
+        rd = mean(cls, "FETCH_SIZE") * 1024.0 / kf if kf and mean(cls, "FETCH_SIZE") is not None else None
+        wr = mean(cls, "WRITE_SIZE") * 1024.0 / kw if kw and mean(cls, "WRITE_SIZE") is not None else None
+        ab = algo.get(cls, {}).get("bytes")
+        tot_ratio = (rd + wr) / ab if rd is not None and wr is not None and ab else None
+        bc, la = mean(cls, "SQ_LDS_BANK_CONFLICT"), mean(cls, "SQ_LDS_IDX_ACTIVE")
+        conf = 100.0 * bc / la if bc is not None and la else None
+        waves = mean(cls, "SQ_WAVES")
+        mix = None
+        if waves:
+            mix = " / ".join(f"{(mean(cls, c) or 0) / waves:.0f}" for c in
+                             ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU"))
+        wc = mean(cls, "SQ_WAVE_CYCLES")
+        waits = None
+        if wc:
+            waits = f"{100 * (mean(cls, 'SQ_WAIT_ANY') or 0) / wc:.0f} / {100 * (mean(cls, 'SQ_WAIT_INST_ANY') or 0) / wc:.0f}"
+        f = lambda x, fmt: "—" if x is None else format(x, fmt)
+        n_disp = len(merged[cls]["duration_ns"])
+        lines.append(f"| {cls} | {n_disp} | {f(dur / 1e3 if dur else None, '.1f')} | {f(clock, '.2f')} "
+                     f"| {f(util, '.1f')} | {f(fl_ratio, '.3f')} | {f(rd / 1e6 if rd is not None else None, '.1f')} "
+                     f"| {f(wr / 1e6 if wr is not None else None, '.1f')} | {f(tot_ratio, '.3f')} "
+                     f"| {f(conf, '.1f')} | {mix or '—'} | {waits or '—'} |")
+        res[cls] = {"util": util, "clock": clock, "rd": rd, "wr": wr, "algo_bytes": ab}
+    lines += ["", "Algorithmic work per launch (the bench's roofline units):"]
+    lines += [f"- indexer_score: {algo['indexer_score']['flop']:.4e} FLOP (16,384 per visible pair, "
+              f"{pairs} pairs); {algo['indexer_score']['bytes']} B (keys once, q, w, scores written)",
+              f"- topk: {algo['topk']['bytes']} B (4 per visible pair read, 4 k per row written)",
+              f"- attention: {algo['attention']['flop']:.4e} FLOP (4 H D per query and key); "
+              f"{algo['attention']['bytes']} B logical (one {D}-dim bf16 row per query and key, "
+              "q and out, the selection)",
+              "", "MFMA busy % = sum of SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1,024 SIMDs): "
+              "the share of SIMD cycles the matrix cores were busy, at the clock the kernel ran at.",
+              "clock = GRBM_GUI_ACTIVE / duration."]
     with open(out_md, "w") as fh:
-        fh.write(f"# HBM traffic of the indexer score kernel, {workload}\n\n")
-        fh.write("Counters: rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each in its own\n"
-                 "run, summed over instances per dispatch and averaged over the score kernel's\n"
-                 "dispatches; each scaled by what the same counter reads for a plain copy kernel of\n"
-                 "known size in the same process (--calibration-copy: a torch elementwise negate\n"
-                 "that reads 1 GiB and writes 1 GiB).\n\n")
-        fh.write("Commands:\n\n```\n" + cmds.strip() + "\n```\n\n")
-        fh.write(f"- workload: `{workload}`\n")
-        fh.write(f"- score_source_hash: `{score_source_hash()}`\n")
-        fh.write(f"- score_dispatches: {len(fs)} (fetch run), {len(ws)} (write run)\n")
-        fh.write(f"- copy_fetch_kib_per_gib: {np.mean(fc):.1f}\n")
-        fh.write(f"- copy_write_kib_per_gib: {np.mean(wc):.1f}\n")
-        fh.write(f"- fetch_scale: {k_fetch:.4f}\n")
-        fh.write(f"- write_scale: {k_write:.4f}\n")
-        fh.write(f"- score_fetch_kib_raw: {np.mean(fs):.1f}\n")
-        fh.write(f"- score_write_kib_raw: {np.mean(ws):.1f}\n")
-        fh.write(f"- hbm_fetch_bytes_per_launch: {fetch_b:.0f}\n")
-        fh.write(f"- hbm_write_bytes_per_launch: {write_b:.0f}\n")
-        fh.write(f"- hbm_bytes_per_launch: {fetch_b + write_b:.0f}\n")
-        fh.write(f"- algorithmic_bytes_per_launch: {algo} (keys once + q + w + score rows "
-                 f"+ T x S scores written; {pairs} visible pairs)\n")
+        fh.write("\n".join(lines) + "\n")
     print(open(out_md).read())
+    sc = res.get("indexer_score")
+    if sc and sc["rd"] is not None and sc["wr"] is not None:
+        with open(traffic_file(workload), "w") as fh:
+            fh.write(f"# HBM traffic of the indexer score kernel, {workload}\n\n")
+            fh.write("FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by the same counter's reading "
+                     "for the 1 GiB probe copy; taken with the counter runs of "
+                     f"`{os.path.basename(out_md)}` (commands there).\n\n")
+            fh.write(f"- workload: `{workload}`\n- score_source_hash: `{score_source_hash()}`\n")
+            fh.write(f"- hbm_fetch_bytes_per_launch: {sc['rd']:.0f}\n")
+            fh.write(f"- hbm_write_bytes_per_launch: {sc['wr']:.0f}\n")
+            fh.write(f"- hbm_bytes_per_launch: {sc['rd'] + sc['wr']:.0f}\n")
+            fh.write(f"- algorithmic_bytes_per_launch: {sc['algo_bytes']}\n")
 
 
 def parse():
@@ -153,10 +247,13 @@ def parse():
                     help="one bench line per named workload (tiny .. 1M), without the extras")
     ap.add_argument("--no-modes", action="store_true",
                     help="skip the sibling-mode and narrow-query measurements")
+    ap.add_argument("--lean", action="store_true",
+                    help="only the timed steps and per-kernel timings (for profiler runs)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after the benchmark, run a 1 GiB copy kernel three times (counter scale)")
-    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "OUT_MD"),
-                    help="write the score kernel's traffic summary from two counter runs and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="ARG",
+                    help="OUT_MD DB [DB ...]: write the counter summary of the hot-path kernels "
+                         "(and the score kernel's traffic file) from rocprofv3 --pmc runs and exit")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DB", "BENCH_LOG", "OUT_MD"),
                     help="write the kernel-trace summary of a profiled bench run and exit")
     ap.add_argument("--commands", default="",
@@ -252,14 +349,57 @@ def per_call_stats(fn, reps: int, scrub=None) -> dict:
     return {"median": float(np.median(times)), "min": float(np.min(times))}
 
 
+def probe_lib():
+    """The ceiling probes (libdsv4_probe.so, built beside libdsv4.so)."""
+    import ctypes
+    path = os.path.join(ROOT, "sparse_indexed_attention_amd", "libdsv4_probe.so")
+    L = ctypes.CDLL(path)
+    L.dsv4_probe_mfma_flops.restype = ctypes.c_double
+    L.dsv4_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.dsv4_probe_mfma.restype = ctypes.c_int
+    L.dsv4_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    L.dsv4_probe_copy.restype = ctypes.c_int
+    L.dsv4_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                  ctypes.c_void_p]
+    return L
+
+
+def probe_copy(L, src, dst, workgroups=4096):
+    rc = L.dsv4_probe_copy(src.data_ptr(), dst.data_ptr(), src.numel() * src.element_size(),
+                           workgroups, torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"copy probe launch failed ({rc})")
+
+
 def achievable_peaks() -> dict:
-    """What this machine reaches with plain library work in the same process: a
-    1 GiB device-to-device copy (2 GiB moved) and a 8192^3 bf16 GEMM
-    (torch.matmul on contiguous operands).  Reported beside the spec peaks."""
+    """What this machine reaches on plain work in the same process:
+    - a register-resident v_mfma_f32_32x32x16_bf16 loop over varied bf16
+      operands (two and four waves per SIMD on every CU), with the engine
+      clock it ran at (shader-clock and 100 MHz counters of one wave);
+    - a 16-byte-per-lane copy of 1 GiB (reads 1 GiB, writes 1 GiB);
+    - for context, an 8192^3 bf16 torch.matmul (hipBLASLt)."""
+    L = probe_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    best = None
+    for wg in (512, 1024):
+        iters = 2000
+        out = torch.empty(wg * 256, device="cuda")
+        stamps = torch.zeros(2, dtype=torch.int64, device="cuda")
+        run = lambda: L.dsv4_probe_mfma(wg, iters, out.data_ptr(), stamps.data_ptr(), stream)
+        if run() != 0:
+            raise RuntimeError("mfma probe launch failed")
+        ms = timed_kernel(run, 5)
+        ticks, real = stamps.cpu().tolist()
+        tflops = L.dsv4_probe_mfma_flops(wg, iters) / (ms * 1e-3) / 1e12
+        rec = {"TFLOPs": tflops, "workgroups": wg, "ms": ms,
+               "clock_GHz": ticks / (real / 1e8) / 1e9 if real > 0 else None}
+        if best is None or tflops > best["TFLOPs"]:
+            best = rec
     n = 1 << 28
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    ms_copy = timed_kernel(lambda: dst.copy_(src), 10)
+    ms_copy = min(timed_kernel(lambda: probe_copy(L, src, dst, wg), 10) for wg in (2048, 8192))
     del src, dst
     m = 8192
     a = torch.randn((m, m), device="cuda").to(torch.bfloat16)
@@ -267,9 +407,11 @@ def achievable_peaks() -> dict:
     ms_gemm = timed_kernel(lambda: torch.matmul(a, b), 10)
     del a, b
     torch.cuda.empty_cache()
-    return {"hbm_copy_GBps": 2 * n * 4 / (ms_copy * 1e-3) / 1e9,
-            "bf16_gemm_TFLOPs": 2 * m ** 3 / (ms_gemm * 1e-3) / 1e12,
-            "how": "1 GiB device copy; 8192^3 bf16 torch.matmul (hipBLASLt), same process"}
+    return {"mfma_loop_bf16_TFLOPs": best["TFLOPs"], "mfma_loop": best,
+            "hbm_copy_GBps": 2 * n * 4 / (ms_copy * 1e-3) / 1e9,
+            "library_gemm_bf16_TFLOPs": 2 * m ** 3 / (ms_gemm * 1e-3) / 1e12,
+            "how": "register-resident 32x32x16 bf16 MFMA loop and 1 GiB 16-byte copy "
+                   "(libdsv4_probe.so); 8192^3 bf16 torch.matmul for context; same process"}
 
 
 def measure_modes(setup: Setup, reps: int) -> dict:
@@ -444,14 +586,29 @@ def tile_matrix(steps: int):
         torch.cuda.empty_cache()
 
 
-def cpu_baseline(setup: Setup, budget_s: float):
-    """The CPU oracle (score + top-k) on a bounded sample of the chunk's query rows."""
-    from oracle import dsv4_oracle as O
+def cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.lower().startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(setup: Setup, budget_s: float):
+    """The CPU oracle (score + top-k) on a bounded sample of the chunk's query
+    rows, on every host core this process may run on (BLAS threads set to
+    that count)."""
+    from oracle import dsv4_oracle as O
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits, threadpool_info
+        limiter = threadpool_limits(limits=cores)
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = 1
+        limiter, threads = None, None
     wl, inp = setup.wl, setup.inp
     S = setup.S_after
     st = O.PoolingCacheState(wl.idx_dim, S)
@@ -469,7 +626,10 @@ def cpu_baseline(setup: Setup, budget_s: float):
         O.topk_select(sc, wl.q_pos0 + t, wl.topk)
         n += 1
     dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "query rows/s", "cores": int(threads), "kind": "oracle",
+    if limiter is not None:
+        limiter.restore_original_limits()
+    return {"value": n / dt, "unit": "query rows/s", "cores": cores, "blas_threads": threads,
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{n} random query rows of the chunk (score + top-k, numpy fp64), {dt:.1f} s"}
 
 
@@ -506,8 +666,9 @@ def main():
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, args.commands)
         return
-    if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc, args.workload, args.commands)
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1:], args.workload,
+                           args.commands)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the hot path runs on one MI355X and this build "
@@ -526,14 +687,15 @@ def main():
             sys.stdout.flush()
             torch.cuda.empty_cache()
         return
-    rec = run_workload(args, SI.WORKLOADS[args.workload], extras=True)
+    rec = run_workload(args, SI.WORKLOADS[args.workload], extras=not args.lean)
     print(json.dumps(rec))
     sys.stdout.flush()
     if args.calibration_copy:
+        L = probe_lib()
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(3):
-            torch.neg(src, out=dst)  # elementwise kernel: reads 1 GiB, writes 1 GiB
+            probe_copy(L, src, dst)  # reads 1 GiB, writes 1 GiB
         torch.cuda.synchronize()
 
 
@@ -620,6 +782,8 @@ def run_workload(args, wl: SI.Workload, extras: bool) -> dict:
             modes = measure_modes(setup, max(5, args.steps // 2))
             narrow = measure_narrow(setup, max(10, args.steps))
     budget = args.cpu_seconds if extras else min(args.cpu_seconds, 4.0)
+    if args.lean:
+        budget = 0
     cpu = cpu_baseline(setup, budget) if budget > 0 else None
     ach = (lambda x, key: x / peaks[key]) if peaks else (lambda x, key: None)
     rec = {
@@ -648,7 +812,7 @@ def run_workload(args, wl: SI.Workload, extras: bool) -> dict:
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": score_tflops / PEAK_BF16_TFLOPS,
                      "traffic": recorded_traffic(wl.name),
-                     "frac_of_achievable": ach(score_tflops, "bf16_gemm_TFLOPs")},
+                     "frac_of_achievable": ach(score_tflops, "mfma_loop_bf16_TFLOPs")},
         "per_call_ms": calls,
         "achievable": peaks,
         "topk_roofline": {"bound": "hbm", "achieved": topk_gbs, "peak": PEAK_HBM_GBS,
@@ -656,7 +820,7 @@ def run_workload(args, wl: SI.Workload, extras: bool) -> dict:
                           "frac_of_achievable": ach(topk_gbs, "hbm_copy_GBps")},
         "attn_roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                           "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                          "frac_of_achievable": ach(attn_tflops, "bf16_gemm_TFLOPs"),
+                          "frac_of_achievable": ach(attn_tflops, "mfma_loop_bf16_TFLOPs"),
                           "gather_GBps": attn_gather / (attn * 1e-3) / 1e9},
         "modes": modes,
         "narrow": narrow,

@@ -3,7 +3,8 @@
     python -m sparse_indexed_attention_amd.build
 
 Each HIP source is compiled to an object for --offload-arch=gfx950, then
-linked into ``sparse_indexed_attention_amd/libdsv4.so`` next to this file.
+linked into ``sparse_indexed_attention_amd/libdsv4.so`` next to this file;
+the benchmark's ceiling probes go into ``libdsv4_probe.so`` beside it.
 Packed-fp32 instruction selection is disabled for every device compile.
 """
 from __future__ import annotations
@@ -19,6 +20,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdsv4.so")
+# ceiling probes for the benchmark (MFMA loop, copy), a library of their own
+PROBE_LIB = os.path.join(HERE, "libdsv4_probe.so")
+PROBE_SOURCES = ["peak_probe.hip"]
 
 DEVICE_SOURCES = ["compress.hip", "indexer_score.hip", "topk.hip", "sparse_attn.hip",
                   "noalloc.hip"]
@@ -56,16 +60,18 @@ def build(verbose: bool = False) -> str:
         jobs.append((os.path.join(CSRC, name), os.path.join(OBJ, name + ".o"), True))
     for name in HOST_SOURCES:
         jobs.append((os.path.join(CSRC, name), os.path.join(OBJ, name + ".o"), False))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
-        for out in ex.map(_compile, jobs):
+    probe_jobs = [(os.path.join(CSRC, n), os.path.join(OBJ, n + ".o"), True) for n in PROBE_SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs) + len(probe_jobs))) as ex:
+        for out in ex.map(_compile, jobs + probe_jobs):
             if verbose and out.strip():
                 print(out)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + [j[1] for j in jobs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    for lib, objs in ((LIB, [j[1] for j in jobs]), (PROBE_LIB, [j[1] for j in probe_jobs])):
+        tmp = lib + ".tmp"
+        cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+        os.replace(tmp, lib)
     return LIB
 
 
