@@ -25,7 +25,7 @@ PROBE_LIB = os.path.join(HERE, "libdsv4_probe.so")
 PROBE_SOURCES = ["peak_probe.hip"]
 
 DEVICE_SOURCES = ["compress.hip", "indexer_score.hip", "topk.hip", "sparse_attn.hip",
-                  "noalloc.hip"]
+                  "attn_h64.hip", "noalloc.hip"]
 HOST_SOURCES = ["dsv4_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}"]

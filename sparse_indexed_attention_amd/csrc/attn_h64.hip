@@ -1,0 +1,429 @@
+// Fused windowed + pooled sparse prefill attention at the hot shape, H = 64
+// heads, D = 512 dims, bf16 MFMA on gfx950.
+//
+// [P2 "perf(deepseek_v4): faster exact DeepSeek-V4 prefill", commit 1: one
+// attention over the sliding raw-token window plus the pooled rows, B=1,
+// H=64, D=512, bf16, masks rebuilt from offsets; P3 "[Discussion] Tile
+// indexed-attention scoring ...", Possible design step 4.]
+//
+// Same definition, arguments and key walk as sparse_attn_kernel (one
+// workgroup per query, 32-key tiles gathered straight into LDS, key slots
+// masked from positions), with a work split chosen for LDS traffic, which
+// bounds the per-head-group layout at this shape: each K element read from
+// LDS there feeds 16 heads, and the transposed V reads (ds_read_b64_tr_b16)
+// move half the bytes per clock of ds_read_b128.  Here, with 8 waves:
+//   * QK^T: wave w = hg + 2 dh + 4 kh computes partial scores S^T (16 keys x
+//     32 heads) for key half kh, head group hg (32 heads), over dim half dh
+//     (256 dims) -- its Q block (32 heads x 256 dims, 64 VGPRs) stays in
+//     registers, and every K fragment read feeds two MFMAs (32 heads);
+//   * the partials of head tile (hg, 1 - dh) go through LDS to the wave that
+//     owns that tile, which adds its own: each (head tile, key half) has one
+//     owner, which runs the online softmax for it and writes P (bf16) to an
+//     LDS tile [head][key];
+//   * P.V: wave w accumulates O for all 64 heads x dims 64w .. 64w+63
+//     (64 VGPRs): every transposed V read feeds four MFMAs (64 heads);
+//   * per 32-key tile, each CU then reads 64 KiB of K, 32 KiB of V, 8 KiB of
+//     partial scores and 32 KiB of P from LDS, against 128 + 128 + 32 KiB
+//     in the per-head-group layout.
+// Softmax: online, fp32, exp2 with the scale folded in, against a per-head
+// reference max that moves lazily.  Each owner computes P against the
+// current reference and flags its heads whose tile max passes it by more
+// than 2^8; the flags cross the next barrier, and only on a flagged tile
+// (the first tile of every query, and rare jumps) do the owners move the
+// reference, rewrite that tile's P and publish the rescale factors, which
+// costs one more barrier.  Otherwise p <= 2^8.
+// Pipeline, two barriers per tile (three LDS stages): iteration t waits for
+// tile t's gather, barrier A (publishes tile t, P(t-1), the flags), checks
+// the flags of t-1, P.V(t-1), QK(t), barrier B (publishes the partials;
+// stage t-1 is free), gathers tile t+2, softmax(t) -> P(t).
+#include "dsv4_device.h"
+
+using namespace dsv4;
+
+namespace {
+
+constexpr int kD = 512;
+constexpr int kH = 64;
+constexpr int kKeys = 32;
+constexpr int kStages = 3;
+constexpr int kNW = 8;
+constexpr int kNT = kNW * 64;
+constexpr int kTileElems = kKeys * kD;
+constexpr int kPStride = 40;          // bf16 per P row: 32 keys + 8 pad (80 B: conflict-free b128)
+constexpr float kSlack = 8.f;         // lazy max slack, log2 units
+constexpr int kInstsPerWave = kKeys / kNW;  // gather instructions per wave per tile (one row each)
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// 16-byte chunk c of tile row r sits at slot c ^ swz(r): r's low 4 bits
+// rotated right by one, a bijection that keeps both the K fragment reads
+// (16 rows, one chunk) and the transposed V reads conflict-free.
+__device__ __forceinline__ int swz(int r) { return ((r & 1) << 3) | ((r >> 1) & 7); }
+
+// max / sum over lanes l, l^16, l^32, l^48 (the four 16-lane rows).
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__global__ void __launch_bounds__(kNT)
+attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2,
+                const uint16_t* __restrict__ raw, int64_t raw_pos0, int window,
+                const uint16_t* __restrict__ pooled, int ratio,
+                const int32_t* __restrict__ sel, int topk, uint16_t* __restrict__ out,
+                int nsplit, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[kStages][kTileElems];
+  __shared__ __attribute__((aligned(16))) float xs[kNW][64 * 4];   // partial scores for the partner
+  __shared__ __attribute__((aligned(16))) uint16_t pbuf[kH * kPStride];
+  __shared__ float s_mx[2][kH];      // per key half: the owner's tile max (log2 units)
+  __shared__ float s_alpha[kH];      // rescale factors of a flagged tile
+  __shared__ float s_l[2][kH];       // per key half: the owner's row sum
+  __shared__ int s_flag[kNW];
+  __shared__ int s_last;
+  extern __shared__ int s_sel[];     // the query's selection row (topk ints)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kb = lane >> 4;
+  const int l16 = lane & 15;
+  // QK / softmax role
+  const int hg = wave & 1;         // head group: heads 32 hg .. 32 hg + 31
+  const int dh = (wave >> 1) & 1;  // dim half of the partial scores; owned head tile
+  const int kh = wave >> 2;        // key half of the tile: keys 16 kh .. 16 kh + 15
+  const int partner = wave ^ 2;    // same heads and keys, other dim half
+  const int own_head = 32 * hg + 16 * dh + l16;
+  // P.V role: dims 64 wave .. 64 wave + 63 of all heads
+
+  int64_t t;
+  {
+    const int64_t nq = gridDim.x, full = nq / 8, rem = nq % 8;
+    const int64_t x = blockIdx.x % 8, r = blockIdx.x / 8;
+    t = x * full + (x < rem ? x : rem) + r;
+  }
+  const int split = blockIdx.y;
+  const int64_t p = q_pos0 + t;
+  const int64_t lo = (p - window + 1) > 0 ? (p - window + 1) : 0;
+  const int n_win = static_cast<int>(p - lo + 1);
+  const int64_t vis = visible_rows(p, ratio);
+  const uint16_t* self_row = raw + (p - raw_pos0) * kD;
+
+  // ---- Q block: B operand of S^T = K.Q^T.  Lane group kb holds dims
+  // 256 dh + 64 kb .. + 63 over the 8 steps (the contraction order is the
+  // same permutation for K below).
+  bf16x8_t qf[2][8];
+  {
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const uint16_t* qp = q + ((t * kH + 32 * hg + 16 * ht + l16) * (int64_t)kD + 256 * dh + 64 * kb);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qf[ht][j] = *reinterpret_cast<const bf16x8_t*>(qp + 8 * j);
+    }
+  }
+
+  int n_slots;
+  if (sel) {
+    if (tid == 0) s_last = -1;
+    __syncthreads();
+    int last = -1;
+    const int32_t* sp = sel + t * topk;
+    for (int j = tid; j < topk; j += kNT) {
+      const int32_t s = sp[j];
+      s_sel[j] = s;
+      if (s >= 0 && s < vis) last = j;
+    }
+    for (int off = 32; off > 0; off >>= 1) last = max(last, __shfl_xor(last, off));
+    if (lane == 0) atomicMax(&s_last, last);
+    __syncthreads();
+    n_slots = s_last + 1;
+  } else {
+    n_slots = static_cast<int>(vis);
+  }
+  const int n_keys = n_win + n_slots;
+  const int n_tiles_all = (n_keys + kKeys - 1) / kKeys;
+  const int tile_lo = static_cast<int>((static_cast<int64_t>(split) * n_tiles_all) / nsplit);
+  const int n_tiles =
+      static_cast<int>((static_cast<int64_t>(split + 1) * n_tiles_all) / nsplit) - tile_lo;
+
+  auto key_row = [&](int j) -> const uint16_t* {
+    if (j < n_win) return raw + (lo + j - raw_pos0) * kD;
+    if (j < n_keys) {
+      const int sl = j - n_win;
+      const int64_t s = sel ? static_cast<int64_t>(s_sel[sl]) : sl;
+      if (s >= 0 && s < vis) return pooled + s * kD;
+    }
+    return nullptr;
+  };
+  struct Look {
+    uint32_t lo, hi, valid;
+  };
+  auto lookup = [&](int tile) -> Look {
+    const uint16_t* rk = lane < kKeys ? key_row(tile * kKeys + lane) : nullptr;
+    Look lk;
+    lk.valid = static_cast<uint32_t>(__ballot(rk != nullptr));
+    const uint64_t ra = reinterpret_cast<uint64_t>(rk ? rk : self_row);
+    lk.lo = static_cast<uint32_t>(ra);
+    lk.hi = static_cast<uint32_t>(ra >> 32);
+    return lk;
+  };
+  // one whole 1 KiB row per wave instruction: rows wave, wave+8, +16, +24
+  auto issue = [&](const Look& lk, int buf) {
+#pragma unroll
+    for (int u = 0; u < kInstsPerWave; ++u) {
+      const int i = wave + kNW * u;
+      const uint64_t base =
+          (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lk.hi), i))) << 32) |
+          static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lk.lo), i));
+      const uint32_t off = static_cast<uint32_t>((lane ^ swz(i)) * 16);
+      global_to_lds16_s(reinterpret_cast<const void*>(base), off, &tiles[buf][i * kD]);
+    }
+  };
+
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the selection are in
+
+  f32x4_t o[4][4];  // [head tile][dim tile]
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) o[a][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY;  // owner: reference max of head own_head
+  float l_part = 0.f;       // owner: row sum of its key half
+  float sv[4];              // owner: the last tile's masked logits (log2 units)
+  float psum = 0.f;         // owner: the last tile's row sum, not yet added
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sv[i] = -INFINITY;
+
+  // A-fragment rows: S^T row m of key half kh is tile key 16 kh + 4 (m % 4)
+  // + m / 4, so the owner's four values (rows 4 kb + i) are keys
+  // 16 kh + 4 i + kb: in P's column order (below) one 8-byte run.
+  const int qk_row = 16 * kh + 4 * (l16 & 3) + (l16 >> 2);
+  const int qk_swz = swz(qk_row);
+  // P.V B-operand rows (transposed reads): keys 4 (l16 / 4) + kb and + 16
+  const int trow0 = 4 * (l16 >> 2) + kb;
+  const int trow1 = 16 + trow0;
+  const int sw0 = swz(trow0), sw1 = swz(trow1);
+  const int dsub = 4 * (l16 & 3);
+  // P is stored [head][column], column 8 b + e holding key 4 e + b: the
+  // k-element e of lane group b in the P.V A operand (whose B operand, read
+  // transposed, holds keys 4 e + b), so each A fragment is one 16-byte read.
+
+  auto qk = [&](int tile, f32x4_t& s0, f32x4_t& s1) {
+    const uint16_t* rb = tiles[tile % kStages] + qk_row * kD;
+    s0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t fa[2][2];
+    auto ld = [&](int j0, int bi) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int chunk = 32 * dh + 8 * kb + j0 + u;
+        fa[bi][u] = *reinterpret_cast<const bf16x8_t*>(rb + ((chunk ^ qk_swz) * 8));
+      }
+    };
+    ld(0, 0);
+#pragma unroll
+    for (int j0 = 0; j0 < 8; j0 += 2) {
+      const int bi = (j0 >> 1) & 1;
+      if (j0 + 2 < 8) ld(j0 + 2, bi ^ 1);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[bi][u], qf[0][j0 + u], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[bi][u], qf[1][j0 + u], s1, 0, 0, 0);
+      }
+    }
+  };
+
+  auto pv = [&](int tile) {
+    const uint16_t* tb = tiles[tile % kStages];
+    bf16x8_t pa[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      pa[a] = *reinterpret_cast<const bf16x8_t*>(&pbuf[(16 * a + l16) * kPStride + 8 * kb]);
+    i16x4_t fv[2][2];
+    auto ld = [&](int n, int bi) {
+      const int d = 64 * wave + 16 * n + dsub;
+      const int ch = d >> 3, off = d & 7;
+      fv[bi][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tb + trow0 * kD + ((ch ^ sw0) * 8) + off));
+      fv[bi][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tb + trow1 * kD + ((ch ^ sw1) * 8) + off));
+    };
+    ld(0, 0);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int bi = n & 1;
+      if (n + 1 < 4) ld(n + 1, bi ^ 1);
+      bf16x8_t b;
+      *reinterpret_cast<i16x4_t*>(&b) = fv[bi][0];
+      *(reinterpret_cast<i16x4_t*>(&b) + 1) = fv[bi][1];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        o[a][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[a], b, o[a][n], 0, 0, 0);
+    }
+  };
+
+  // P values of the owner's four keys against reference m (m = -inf: 0)
+  auto write_p = [&](float m) {
+    const float mu = (m == -INFINITY) ? 0.f : m;
+    float pr[4];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[i] = __builtin_amdgcn_exp2f(sv[i] - mu);
+      s += pr[i];
+    }
+    uint2 w;
+    w.x = pack_bf16x2(pr[0], pr[1]);
+    w.y = pack_bf16x2(pr[2], pr[3]);
+    *reinterpret_cast<uint2*>(&pbuf[own_head * kPStride + 8 * kb + 4 * kh]) = w;
+    psum = rows_sum(s);
+  };
+
+  if (n_tiles > 0) {
+    Look lk = lookup(tile_lo);
+    issue(lk, 0);
+    uint32_t vm_cur = lk.valid, vm_next = 0u;
+    if (n_tiles > 1) {
+      lk = lookup(tile_lo + 1);
+      issue(lk, 1);
+      vm_next = lk.valid;
+    }
+    if (n_tiles > 2) lk = lookup(tile_lo + 2);
+    for (int it = 0; it <= n_tiles; ++it) {
+      if (it < n_tiles) {
+        // this wave's rows of tile `it` landed (tile it+1 may still fly)
+        if (it + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0F70 | kInstsPerWave);
+        else __builtin_amdgcn_s_waitcnt(0x0F70);
+      }
+      __syncthreads();  // A: tile `it`, P(it-1) and its flags are visible
+      if (it >= 1) {
+        // ---- flags of tile it-1: move the references where a tile max
+        // passed them by more than the slack (uniform decision)
+        int any = 0;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) any |= s_flag[w];
+        if (any) {
+          const float tmax = fmaxf(s_mx[0][own_head], s_mx[1][own_head]);
+          const bool bump = tmax > m_ref + kSlack;
+          const float m_new = bump ? tmax : m_ref;
+          const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+          if (kh == 0 && kb == 0) s_alpha[own_head] = alpha;
+          if (__ballot(bump)) write_p(m_new);  // heads without a bump rewrite the same P
+          l_part = l_part * alpha + psum;
+          m_ref = m_new;
+          __syncthreads();  // rewritten P and the factors are visible
+          float al[4][4];
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) al[a][i] = s_alpha[16 * a + 4 * kb + i];
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) o[a][n][i] *= al[a][i];
+        } else {
+          l_part += psum;
+        }
+        pv(it - 1);
+      }
+      if (it < n_tiles) {
+        f32x4_t s0, s1;
+        qk(it, s0, s1);
+        // the partner owns the other head tile of these keys
+        *reinterpret_cast<f32x4_t*>(&xs[wave][lane * 4]) = dh ? s0 : s1;
+        __syncthreads();  // B: partials visible; every wave is done with tile it-1
+        uint32_t vm_after = 0u;
+        if (it + 2 < n_tiles) {
+          issue(lk, (it + 2) % kStages);
+          vm_after = lk.valid;
+          if (it + 3 < n_tiles) lk = lookup(tile_lo + it + 3);
+        }
+        // ---- softmax of the owned (head tile, key half): rows 4 kb + i are
+        // keys 16 kh + 4 i + kb
+        const f32x4_t mine = dh ? s1 : s0;
+        const f32x4_t other = *reinterpret_cast<const f32x4_t*>(&xs[partner][lane * 4]);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 16 * kh + 4 * i + kb;
+          sv[i] = ((vm_cur >> key) & 1u) ? (mine[i] + other[i]) * scale_log2 : -INFINITY;
+          mx = fmaxf(mx, sv[i]);
+        }
+        mx = rows_max(mx);
+        if (kb == 0) s_mx[kh][own_head] = mx;
+        const bool flag = __ballot(mx > m_ref + kSlack) != 0;
+        if (lane == 0) s_flag[wave] = flag ? 1 : 0;
+        write_p(m_ref);
+        vm_cur = vm_next;
+        vm_next = vm_after;
+      }
+    }
+  }
+
+  // ---- row sums of the two key halves, then O normalised (or the split's
+  // partial state)
+  if (kb == 0) s_l[kh][own_head] = l_part;
+  __syncthreads();  // also: every wave is done with the tile stages
+  if (nsplit > 1) {
+    float* po = part_o + ((t * nsplit + split) * kH) * static_cast<int64_t>(kD);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = 16 * a + 4 * kb + i;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) po[hh * static_cast<int64_t>(kD) + 64 * wave + 16 * n + l16] = o[a][n][i];
+      }
+    if (kh == 0 && kb == 0) {
+      part_ml[((t * nsplit + split) * kH + own_head) * 2] = m_ref;
+      part_ml[((t * nsplit + split) * kH + own_head) * 2 + 1] = s_l[0][own_head] + s_l[1][own_head];
+    }
+    return;
+  }
+  uint16_t* stage = &tiles[0][0] + wave * (kH * 64);  // this wave's 64 heads x 64 dims
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = 16 * a + 4 * kb + i;
+      const float l = s_l[0][hh] + s_l[1][hh];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) stage[hh * 64 + 16 * n + l16] = bf16_rne(o[a][n][i] * inv);
+    }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+  __builtin_amdgcn_wave_barrier();
+  // 64 heads x 8 chunks of 16 B per wave
+#pragma unroll
+  for (int c0 = 0; c0 < 8; ++c0) {
+    const int c = c0 * 64 + lane;
+    const int hh = c >> 3, ch = c & 7;
+    *reinterpret_cast<u32x4_t*>(out + (t * kH + hh) * (int64_t)kD + 64 * wave + 8 * ch) =
+        *reinterpret_cast<const u32x4_t*>(stage + hh * 64 + 8 * ch);
+  }
+}
+
+}  // namespace
+
+// Launch of the H = 64, D = 512 kernel (arguments as dsv4_launch_sparse_attn).
+hipError_t dsv4_launch_sparse_attn_h64(const void* q, int64_t T, int64_t q_pos0, float scale_log2,
+                                       const void* raw_kv, int64_t raw_pos0, int32_t window,
+                                       const void* pooled, int32_t ratio, const int32_t* sel_idx,
+                                       int32_t topk, void* out, int32_t nsplit, float* part_o,
+                                       float* part_ml, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>(nsplit));
+  const size_t dyn = static_cast<size_t>(sel_idx ? topk : 0) * sizeof(int);
+  hipLaunchKernelGGL(attn_h64_kernel, grid, dim3(kNT), dyn, s, static_cast<const uint16_t*>(q),
+                     q_pos0, scale_log2, static_cast<const uint16_t*>(raw_kv), raw_pos0, window,
+                     static_cast<const uint16_t*>(pooled), ratio, sel_idx, topk,
+                     static_cast<uint16_t*>(out), nsplit, part_o, part_ml);
+  return hipGetLastError();
+}

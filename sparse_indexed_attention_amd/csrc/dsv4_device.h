@@ -82,10 +82,15 @@ __device__ __forceinline__ int64_t visible_rows(int64_t p, int ratio) {
 // the barrier that publishes the data.  The LDS address goes in m0 as an
 // operand, so the compiler sets m0 itself and knows it is in use.  Issued after the compiler's own loads,
 // these can only make the compiler's in-order vmcnt waits stricter.
+// The compiler does not insert hazard wait states across an inline-asm
+// boundary, so the asm carries its own s_nop 4 (five wait states): an SALU
+// write of m0 needs one before a load into LDS reads it, and a VALU write of
+// an SGPR (v_readlane / v_readfirstlane making the base or m0) needs five
+// before a vector-memory instruction reads that SGPR.
 __device__ __forceinline__ void global_to_lds16(const void* g, const void* lds_wave_base) {
   const uint32_t lds = static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_wave_base));
-  asm volatile("global_load_lds_dwordx4 %0, off"
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");
@@ -97,7 +102,7 @@ __device__ __forceinline__ void global_to_lds16_s(const void* sbase, uint32_t vo
                                                   const void* lds_wave_base) {
   const uint32_t lds = static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_wave_base));
-  asm volatile("global_load_lds_dwordx4 %0, %1"
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");
@@ -148,6 +153,12 @@ hipError_t dsv4_launch_sparse_attn(const void* q, int64_t T, int64_t q_pos0, int
                                    int32_t ratio, const int32_t* sel_idx, int32_t topk,
                                    void* out, int32_t nsplit, float* part_o, float* part_ml,
                                    hipStream_t s);
+// The H = 64, D = 512 kernel (attn_h64.hip); scale_log2 = scale * log2(e).
+hipError_t dsv4_launch_sparse_attn_h64(const void* q, int64_t T, int64_t q_pos0, float scale_log2,
+                                       const void* raw_kv, int64_t raw_pos0, int32_t window,
+                                       const void* pooled, int32_t ratio, const int32_t* sel_idx,
+                                       int32_t topk, void* out, int32_t nsplit, float* part_o,
+                                       float* part_ml, hipStream_t s);
 hipError_t dsv4_launch_attn_combine(const float* part_o, const float* part_ml, int64_t T,
                                     int32_t nsplit, int32_t n_heads, int32_t head_dim, void* out,
                                     hipStream_t s);

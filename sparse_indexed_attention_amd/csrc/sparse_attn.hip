@@ -596,6 +596,9 @@ hipError_t dsv4_launch_sparse_attn(const void* q, int64_t T, int64_t q_pos0, int
   if (T <= 0) return hipSuccess;
   if (nsplit < 1) return hipErrorInvalidValue;
   const float sl2 = scale * 1.4426950408889634f;
+  if (head_dim == 512 && n_heads == 64)
+    return dsv4_launch_sparse_attn_h64(q, T, q_pos0, sl2, raw_kv, raw_pos0, window, pooled, ratio,
+                                       sel_idx, topk, out, nsplit, part_o, part_ml, s);
   switch (head_dim) {
     case 32: return launch_d<32>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, ratio, sel_idx, topk, out, nsplit, part_o, part_ml, s);
     case 64: return launch_d<64>(q, T, q_pos0, n_heads, sl2, raw_kv, raw_pos0, window, pooled, ratio, sel_idx, topk, out, nsplit, part_o, part_ml, s);
