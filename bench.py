@@ -85,7 +85,8 @@ def recorded_traffic(workload: str):
 
 
 KERNEL_CLASSES = (("indexer_score", "indexer_score_kernel"), ("topk", "topk_reg_kernel"),
-                  ("attention", "sparse_attn_kernel"), ("compress", "compress_kernel"),
+                  ("attention", "sparse_attn_kernel"), ("attention", "attn_h64_kernel"),
+                  ("compress", "compress_kernel"),
                   ("copy", "copy_kernel"))
 
 

@@ -36,6 +36,8 @@
 // tile t's gather, barrier A (publishes tile t, P(t-1), the flags), checks
 // the flags of t-1, P.V(t-1), QK(t), barrier B (publishes the partials;
 // stage t-1 is free), gathers tile t+2, softmax(t) -> P(t).
+#include <type_traits>
+
 #include "dsv4_device.h"
 
 using namespace dsv4;
@@ -85,7 +87,7 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
   __shared__ __attribute__((aligned(16))) float xs[kNW][64 * 4];   // partial scores for the partner
   __shared__ __attribute__((aligned(16))) uint16_t pbuf[kH * kPStride];
   __shared__ float s_mx[2][kH];      // per key half: the owner's tile max (log2 units)
-  __shared__ float s_alpha[kH];      // rescale factors of a flagged tile
+  __shared__ __attribute__((aligned(16))) float s_alpha[kH];  // rescale factors of a flagged tile
   __shared__ float s_l[2][kH];       // per key half: the owner's row sum
   __shared__ int s_flag[kNW];
   __shared__ int s_last;
@@ -216,8 +218,8 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
   // k-element e of lane group b in the P.V A operand (whose B operand, read
   // transposed, holds keys 4 e + b), so each A fragment is one 16-byte read.
 
-  auto qk = [&](int tile, f32x4_t& s0, f32x4_t& s1) {
-    const uint16_t* rb = tiles[tile % kStages] + qk_row * kD;
+  auto qk = [&](auto stage, f32x4_t& s0, f32x4_t& s1) {
+    const uint16_t* rb = tiles[decltype(stage)::value] + qk_row * kD;
     s0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
     s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
     bf16x8_t fa[2][2];
@@ -241,8 +243,8 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
     }
   };
 
-  auto pv = [&](int tile) {
-    const uint16_t* tb = tiles[tile % kStages];
+  auto pv = [&](auto stage) {
+    const uint16_t* tb = tiles[decltype(stage)::value];
     bf16x8_t pa[4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -295,7 +297,12 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
       vm_next = lk.valid;
     }
     if (n_tiles > 2) lk = lookup(tile_lo + 2);
-    for (int it = 0; it <= n_tiles; ++it) {
+    // One iteration; the loop below is unrolled over the three stages, so
+    // every LDS address is a lane base plus an immediate.  `st` is
+    // it % kStages; tile it-1 (and tile it+2) sit in stage (st + 2) % 3.
+    auto step = [&](auto st, int it) {
+      constexpr int S = decltype(st)::value;
+      constexpr int SP = (S + 2) % kStages;
       if (it < n_tiles) {
         // this wave's rows of tile `it` landed (tile it+1 may still fly)
         if (it + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0F70 | kInstsPerWave);
@@ -308,41 +315,36 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
         int any = 0;
 #pragma unroll
         for (int w = 0; w < kNW; ++w) any |= s_flag[w];
-        if (any) {
+        if (__builtin_expect(any, 0)) {
           const float tmax = fmaxf(s_mx[0][own_head], s_mx[1][own_head]);
           const bool bump = tmax > m_ref + kSlack;
           const float m_new = bump ? tmax : m_ref;
           const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
           if (kh == 0 && kb == 0) s_alpha[own_head] = alpha;
           if (__ballot(bump)) write_p(m_new);  // heads without a bump rewrite the same P
-          l_part = l_part * alpha + psum;
+          psum = l_part * alpha + psum;        // the new row sum, added below
+          l_part = 0.f;
           m_ref = m_new;
           __syncthreads();  // rewritten P and the factors are visible
-          float al[4][4];
 #pragma unroll
-          for (int a = 0; a < 4; ++a)
+          for (int a = 0; a < 4; ++a) {
+            const f32x4_t al = *reinterpret_cast<const f32x4_t*>(&s_alpha[16 * a + 4 * kb]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) al[a][i] = s_alpha[16 * a + 4 * kb + i];
-#pragma unroll
-          for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int n = 0; n < 4; ++n)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) o[a][n][i] *= al[a][i];
-        } else {
-          l_part += psum;
+            for (int n = 0; n < 4; ++n) o[a][n] *= al;
+          }
         }
-        pv(it - 1);
+        l_part += psum;
+        pv(std::integral_constant<int, SP>{});
       }
       if (it < n_tiles) {
         f32x4_t s0, s1;
-        qk(it, s0, s1);
+        qk(std::integral_constant<int, S>{}, s0, s1);
         // the partner owns the other head tile of these keys
         *reinterpret_cast<f32x4_t*>(&xs[wave][lane * 4]) = dh ? s0 : s1;
         __syncthreads();  // B: partials visible; every wave is done with tile it-1
         uint32_t vm_after = 0u;
         if (it + 2 < n_tiles) {
-          issue(lk, (it + 2) % kStages);
+          issue(lk, SP);
           vm_after = lk.valid;
           if (it + 3 < n_tiles) lk = lookup(tile_lo + it + 3);
         }
@@ -365,6 +367,13 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
         vm_cur = vm_next;
         vm_next = vm_after;
       }
+    };
+    for (int it = 0; it <= n_tiles; it += kStages) {
+      step(std::integral_constant<int, 0>{}, it);
+      if (it + 1 > n_tiles) break;
+      step(std::integral_constant<int, 1>{}, it + 1);
+      if (it + 2 > n_tiles) break;
+      step(std::integral_constant<int, 2>{}, it + 2);
     }
   }
 
