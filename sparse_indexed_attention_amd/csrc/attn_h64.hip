@@ -47,7 +47,7 @@ namespace {
 constexpr int kD = 512;
 constexpr int kH = 64;
 constexpr int kKeys = 32;
-constexpr int kStages = 3;
+constexpr int kStages = 4;
 constexpr int kNW = 8;
 constexpr int kNT = kNW * 64;
 constexpr int kTileElems = kKeys * kD;
@@ -85,7 +85,7 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
                 int nsplit, float* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(16))) uint16_t tiles[kStages][kTileElems];
   __shared__ __attribute__((aligned(16))) float xs[kNW][64 * 4];   // partial scores for the partner
-  __shared__ __attribute__((aligned(16))) uint16_t pbuf[kH * kPStride];
+  __shared__ __attribute__((aligned(16))) uint16_t pbuf[2][kH * kPStride];  // P, by tile parity
   __shared__ float s_mx[2][kH];      // per key half: the owner's tile max (log2 units)
   __shared__ __attribute__((aligned(16))) float s_alpha[kH];  // rescale factors of a flagged tile
   __shared__ float s_l[2][kH];       // per key half: the owner's row sum
@@ -243,12 +243,13 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
     }
   };
 
-  auto pv = [&](auto stage) {
+  auto pv = [&](auto stage, auto par) {
     const uint16_t* tb = tiles[decltype(stage)::value];
+    const uint16_t* pb = pbuf[decltype(par)::value];
     bf16x8_t pa[4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
-      pa[a] = *reinterpret_cast<const bf16x8_t*>(&pbuf[(16 * a + l16) * kPStride + 8 * kb]);
+      pa[a] = *reinterpret_cast<const bf16x8_t*>(&pb[(16 * a + l16) * kPStride + 8 * kb]);
     i16x4_t fv[2][2];
     auto ld = [&](int n, int bi) {
       const int d = 64 * wave + 16 * n + dsub;
@@ -271,7 +272,7 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
   };
 
   // P values of the owner's four keys against reference m (m = -inf: 0)
-  auto write_p = [&](float m) {
+  auto write_p = [&](float m, auto par) {
     const float mu = (m == -INFINITY) ? 0.f : m;
     float pr[4];
     float s = 0.f;
@@ -283,7 +284,7 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
     uint2 w;
     w.x = pack_bf16x2(pr[0], pr[1]);
     w.y = pack_bf16x2(pr[2], pr[3]);
-    *reinterpret_cast<uint2*>(&pbuf[own_head * kPStride + 8 * kb + 4 * kh]) = w;
+    *reinterpret_cast<uint2*>(&pbuf[decltype(par)::value][own_head * kPStride + 8 * kb + 4 * kh]) = w;
     psum = rows_sum(s);
   };
 
@@ -297,22 +298,35 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
       vm_next = lk.valid;
     }
     if (n_tiles > 2) lk = lookup(tile_lo + 2);
-    // One iteration; the loop below is unrolled over the three stages, so
-    // every LDS address is a lane base plus an immediate.  `st` is
-    // it % kStages; tile it-1 (and tile it+2) sit in stage (st + 2) % 3.
+    // Iteration `it` (the loop below is unrolled over the four stages, so
+    // every LDS address is a lane base plus an immediate; `st` is
+    // it % kStages, and the P parity it % 2 follows):
+    //   wait for tile it's rows; barrier A (tile it, P(it-1), the flags of
+    //   it-1; stage it-2 is free); gather tile it+2; settle the flags of
+    //   it-1 (owners move references, rewrite P(it-1), publish factors);
+    //   QK(it) -> partials; barrier B; then softmax(it) -> P(it) beside
+    //   P.V(it-1), which need no barrier between them.
     auto step = [&](auto st, int it) {
       constexpr int S = decltype(st)::value;
-      constexpr int SP = (S + 2) % kStages;
+      constexpr int SP = (S + kStages - 1) % kStages;  // tile it-1
+      constexpr int SN = (S + 2) % kStages;            // tile it+2
+      constexpr int PAR = S & 1, PARP = PAR ^ 1;      // P of tile it, of it-1
       if (it < n_tiles) {
         // this wave's rows of tile `it` landed (tile it+1 may still fly)
         if (it + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0F70 | kInstsPerWave);
         else __builtin_amdgcn_s_waitcnt(0x0F70);
       }
-      __syncthreads();  // A: tile `it`, P(it-1) and its flags are visible
+      __syncthreads();  // A
+      uint32_t vm_after = 0u;
+      if (it + 2 < n_tiles) {
+        issue(lk, SN);
+        vm_after = lk.valid;
+        if (it + 3 < n_tiles) lk = lookup(tile_lo + it + 3);
+      }
+      int any = 0;
       if (it >= 1) {
         // ---- flags of tile it-1: move the references where a tile max
         // passed them by more than the slack (uniform decision)
-        int any = 0;
 #pragma unroll
         for (int w = 0; w < kNW; ++w) any |= s_flag[w];
         if (__builtin_expect(any, 0)) {
@@ -321,33 +335,30 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
           const float m_new = bump ? tmax : m_ref;
           const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
           if (kh == 0 && kb == 0) s_alpha[own_head] = alpha;
-          if (__ballot(bump)) write_p(m_new);  // heads without a bump rewrite the same P
-          psum = l_part * alpha + psum;        // the new row sum, added below
+          // heads without a bump rewrite the same P
+          if (__ballot(bump)) write_p(m_new, std::integral_constant<int, PARP>{});
+          psum = l_part * alpha + psum;
           l_part = 0.f;
           m_ref = m_new;
-          __syncthreads();  // rewritten P and the factors are visible
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const f32x4_t al = *reinterpret_cast<const f32x4_t*>(&s_alpha[16 * a + 4 * kb]);
-#pragma unroll
-            for (int n = 0; n < 4; ++n) o[a][n] *= al;
-          }
         }
         l_part += psum;
-        pv(std::integral_constant<int, SP>{});
       }
+      f32x4_t s0, s1;
       if (it < n_tiles) {
-        f32x4_t s0, s1;
         qk(std::integral_constant<int, S>{}, s0, s1);
         // the partner owns the other head tile of these keys
         *reinterpret_cast<f32x4_t*>(&xs[wave][lane * 4]) = dh ? s0 : s1;
-        __syncthreads();  // B: partials visible; every wave is done with tile it-1
-        uint32_t vm_after = 0u;
-        if (it + 2 < n_tiles) {
-          issue(lk, SP);
-          vm_after = lk.valid;
-          if (it + 3 < n_tiles) lk = lookup(tile_lo + it + 3);
+      }
+      __syncthreads();  // B: partials, P(it-1) as settled, the factors
+      if (__builtin_expect(any, 0)) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4_t al = *reinterpret_cast<const f32x4_t*>(&s_alpha[16 * a + 4 * kb]);
+#pragma unroll
+          for (int n = 0; n < 4; ++n) o[a][n] *= al;
         }
+      }
+      if (it < n_tiles) {
         // ---- softmax of the owned (head tile, key half): rows 4 kb + i are
         // keys 16 kh + 4 i + kb
         const f32x4_t mine = dh ? s1 : s0;
@@ -363,10 +374,11 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
         if (kb == 0) s_mx[kh][own_head] = mx;
         const bool flag = __ballot(mx > m_ref + kSlack) != 0;
         if (lane == 0) s_flag[wave] = flag ? 1 : 0;
-        write_p(m_ref);
-        vm_cur = vm_next;
-        vm_next = vm_after;
+        write_p(m_ref, std::integral_constant<int, PAR>{});
       }
+      if (it >= 1) pv(std::integral_constant<int, SP>{}, std::integral_constant<int, PARP>{});
+      vm_cur = vm_next;
+      vm_next = vm_after;
     };
     for (int it = 0; it <= n_tiles; it += kStages) {
       step(std::integral_constant<int, 0>{}, it);
@@ -374,6 +386,8 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
       step(std::integral_constant<int, 1>{}, it + 1);
       if (it + 2 > n_tiles) break;
       step(std::integral_constant<int, 2>{}, it + 2);
+      if (it + 3 > n_tiles) break;
+      step(std::integral_constant<int, 3>{}, it + 3);
     }
   }
 
@@ -421,6 +435,17 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
 }
 
 }  // namespace
+
+// Whether the kernel's LDS (static arrays + the selection row, topk ints)
+// fits a workgroup's 160 KiB: up to k = 3,255 selected slots.
+bool dsv4_attn_h64_fits(int32_t topk) {
+  constexpr size_t kStatic = sizeof(uint16_t) * kStages * kTileElems   // tiles
+                             + sizeof(float) * kNW * 64 * 4           // xs
+                             + sizeof(uint16_t) * 2 * kH * kPStride   // pbuf
+                             + sizeof(float) * (2 * kH + kH + 2 * kH) // s_mx, s_alpha, s_l
+                             + sizeof(int) * (kNW + 1);               // s_flag, s_last
+  return kStatic + sizeof(int) * static_cast<size_t>(topk) <= 160 * 1024;
+}
 
 // Launch of the H = 64, D = 512 kernel (arguments as dsv4_launch_sparse_attn).
 hipError_t dsv4_launch_sparse_attn_h64(const void* q, int64_t T, int64_t q_pos0, float scale_log2,

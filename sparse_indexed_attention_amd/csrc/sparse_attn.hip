@@ -596,7 +596,7 @@ hipError_t dsv4_launch_sparse_attn(const void* q, int64_t T, int64_t q_pos0, int
   if (T <= 0) return hipSuccess;
   if (nsplit < 1) return hipErrorInvalidValue;
   const float sl2 = scale * 1.4426950408889634f;
-  if (head_dim == 512 && n_heads == 64)
+  if (head_dim == 512 && n_heads == 64 && dsv4_attn_h64_fits(sel_idx ? topk : 0))
     return dsv4_launch_sparse_attn_h64(q, T, q_pos0, sl2, raw_kv, raw_pos0, window, pooled, ratio,
                                        sel_idx, topk, out, nsplit, part_o, part_ml, s);
   switch (head_dim) {
