@@ -165,28 +165,34 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
     }
     return nullptr;
   };
+  // Row lookup of two tiles at once: lane k < 32 finds key slot k of
+  // `tile`, lane 32 + k slot k of tile + 1; the ballot's low and high words
+  // are the two tiles' validity masks (bit k: slot k has a row).
   struct Look {
-    uint32_t lo, hi, valid;
+    uint32_t lo, hi;
+    uint64_t valid;
   };
   auto lookup = [&](int tile) -> Look {
-    const uint16_t* rk = lane < kKeys ? key_row(tile * kKeys + lane) : nullptr;
+    const uint16_t* rk = key_row(tile * kKeys + lane);
     Look lk;
-    lk.valid = static_cast<uint32_t>(__ballot(rk != nullptr));
+    lk.valid = __ballot(rk != nullptr);
     const uint64_t ra = reinterpret_cast<uint64_t>(rk ? rk : self_row);
     lk.lo = static_cast<uint32_t>(ra);
     lk.hi = static_cast<uint32_t>(ra >> 32);
     return lk;
   };
   // one whole 1 KiB row per wave instruction: rows wave, wave+8, +16, +24
-  auto issue = [&](const Look& lk, int buf) {
+  // of the lookup's tile `half` (0: its first tile, 1: the second)
+  auto issue = [&](const Look& lk, int buf, int half) {
 #pragma unroll
     for (int u = 0; u < kInstsPerWave; ++u) {
-      const int i = wave + kNW * u;
+      const int i = wave + kNW * u + kKeys * half;
       const uint64_t base =
           (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lk.hi), i))) << 32) |
           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lk.lo), i));
-      const uint32_t off = static_cast<uint32_t>((lane ^ swz(i)) * 16);
-      global_to_lds16_s(reinterpret_cast<const void*>(base), off, &tiles[buf][i * kD]);
+      const int r = i & (kKeys - 1);
+      const uint32_t off = static_cast<uint32_t>((lane ^ swz(r)) * 16);
+      global_to_lds16_s(reinterpret_cast<const void*>(base), off, &tiles[buf][r * kD]);
     }
   };
 
@@ -289,15 +295,14 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
   };
 
   if (n_tiles > 0) {
-    Look lk = lookup(tile_lo);
-    issue(lk, 0);
-    uint32_t vm_cur = lk.valid, vm_next = 0u;
+    Look lk = lookup(tile_lo);  // tiles 0 and 1
+    issue(lk, 0, 0);
+    uint32_t vm_cur = static_cast<uint32_t>(lk.valid), vm_next = 0u;
     if (n_tiles > 1) {
-      lk = lookup(tile_lo + 1);
-      issue(lk, 1);
-      vm_next = lk.valid;
+      issue(lk, 1, 1);
+      vm_next = static_cast<uint32_t>(lk.valid >> 32);
     }
-    if (n_tiles > 2) lk = lookup(tile_lo + 2);
+    if (n_tiles > 2) lk = lookup(tile_lo + 2);  // tiles 2 and 3
     // Iteration `it` (the loop below is unrolled over the four stages, so
     // every LDS address is a lane base plus an immediate; `st` is
     // it % kStages, and the P parity it % 2 follows):
@@ -319,9 +324,10 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
       __syncthreads();  // A
       uint32_t vm_after = 0u;
       if (it + 2 < n_tiles) {
-        issue(lk, SN);
-        vm_after = lk.valid;
-        if (it + 3 < n_tiles) lk = lookup(tile_lo + it + 3);
+        // tile it+2 is the lookup's first tile when it is even, else its second
+        issue(lk, SN, S & 1);
+        vm_after = static_cast<uint32_t>(lk.valid >> (32 * (S & 1)));
+        if ((S & 1) && it + 3 < n_tiles) lk = lookup(tile_lo + it + 3);
       }
       int any = 0;
       if (it >= 1) {
