@@ -90,7 +90,7 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
   __shared__ __attribute__((aligned(16))) float s_alpha[kH];  // rescale factors of a flagged tile
   __shared__ float s_l[2][kH];       // per key half: the owner's row sum
   __shared__ int s_flag[kNW];
-  __shared__ int s_last;
+  __shared__ int s_lastw[kNW];  // per wave: its last visible selection slot
   extern __shared__ int s_sel[];     // the query's selection row (topk ints)
 
   const int tid = threadIdx.x;
@@ -134,19 +134,34 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
 
   int n_slots;
   if (sel) {
-    if (tid == 0) s_last = -1;
-    __syncthreads();
-    int last = -1;
+    // the selection row straight into LDS, 64 slots per wave instruction,
+    // in flight with the Q loads
     const int32_t* sp = sel + t * topk;
-    for (int j = tid; j < topk; j += kNT) {
-      const int32_t s = sp[j];
-      s_sel[j] = s;
-      if (s >= 0 && s < vis) last = j;
+    for (int c = wave; c * 64 < topk; c += kNW) {
+      const int j = c * 64 + lane;
+      if (j < topk) global_to_lds4(sp + j, &s_sel[c * 64]);
     }
-    for (int off = 32; off > 0; off >>= 1) last = max(last, __shfl_xor(last, off));
-    if (lane == 0) atomicMax(&s_last, last);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    n_slots = s_last + 1;
+    // trailing slots that name no visible row are dropped: the last
+    // visible slot of this wave's share, then the largest over the waves
+    int last = -1;
+    for (int i = 0; i * kNT < topk; ++i) {
+      const int j = i * kNT + tid;
+      bool v = false;
+      if (j < topk) {
+        const int32_t s = s_sel[j];
+        v = s >= 0 && s < vis;
+      }
+      const uint64_t b = __ballot(v);
+      if (b) last = i * kNT + wave * 64 + 63 - __builtin_clzll(b);
+    }
+    s_lastw[wave] = last;  // wave-uniform
+    __syncthreads();
+    last = s_lastw[0];
+#pragma unroll
+    for (int w = 1; w < kNW; ++w) last = max(last, s_lastw[w]);
+    n_slots = last + 1;
   } else {
     n_slots = static_cast<int>(vis);
   }
@@ -183,9 +198,9 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
   };
   // one whole 1 KiB row per wave instruction: rows wave, wave+8, +16, +24
   // of the lookup's tile `half` (0: its first tile, 1: the second)
-  auto issue = [&](const Look& lk, int buf, int half) {
+  auto issue = [&](const Look& lk, int buf, int half, int u0, int u1) {
 #pragma unroll
-    for (int u = 0; u < kInstsPerWave; ++u) {
+    for (int u = u0; u < u1; ++u) {
       const int i = wave + kNW * u + kKeys * half;
       const uint64_t base =
           (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lk.hi), i))) << 32) |
@@ -224,8 +239,16 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
   // k-element e of lane group b in the P.V A operand (whose B operand, read
   // transposed, holds keys 4 e + b), so each A fragment is one 16-byte read.
 
+  // The swizzle terms pass through an empty asm at each use, so the compiler
+  // forms the few swizzled LDS addresses of a tile when it needs them rather
+  // than keeping some thirty of them live across the loop.
+  auto opaque = [](int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+  };
   auto qk = [&](auto stage, f32x4_t& s0, f32x4_t& s1) {
     const uint16_t* rb = tiles[decltype(stage)::value] + qk_row * kD;
+    const int q_swz = opaque(qk_swz);
     s0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
     s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
     bf16x8_t fa[2][2];
@@ -233,7 +256,7 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int chunk = 32 * dh + 8 * kb + j0 + u;
-        fa[bi][u] = *reinterpret_cast<const bf16x8_t*>(rb + ((chunk ^ qk_swz) * 8));
+        fa[bi][u] = *reinterpret_cast<const bf16x8_t*>(rb + ((chunk ^ q_swz) * 8));
       }
     };
     ld(0, 0);
@@ -252,6 +275,7 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
   auto pv = [&](auto stage, auto par) {
     const uint16_t* tb = tiles[decltype(stage)::value];
     const uint16_t* pb = pbuf[decltype(par)::value];
+    const int s0w = opaque(sw0), s1w = opaque(sw1);
     bf16x8_t pa[4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -260,8 +284,8 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
     auto ld = [&](int n, int bi) {
       const int d = 64 * wave + 16 * n + dsub;
       const int ch = d >> 3, off = d & 7;
-      fv[bi][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tb + trow0 * kD + ((ch ^ sw0) * 8) + off));
-      fv[bi][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tb + trow1 * kD + ((ch ^ sw1) * 8) + off));
+      fv[bi][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tb + trow0 * kD + ((ch ^ s0w) * 8) + off));
+      fv[bi][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tb + trow1 * kD + ((ch ^ s1w) * 8) + off));
     };
     ld(0, 0);
 #pragma unroll
@@ -296,45 +320,56 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
 
   if (n_tiles > 0) {
     Look lk = lookup(tile_lo);  // tiles 0 and 1
-    issue(lk, 0, 0);
+    issue(lk, 0, 0, 0, kInstsPerWave);
     uint32_t vm_cur = static_cast<uint32_t>(lk.valid), vm_next = 0u;
     if (n_tiles > 1) {
-      issue(lk, 1, 1);
+      issue(lk, 1, 1, 0, kInstsPerWave);
       vm_next = static_cast<uint32_t>(lk.valid >> 32);
     }
     if (n_tiles > 2) lk = lookup(tile_lo + 2);  // tiles 2 and 3
-    // Iteration `it` (the loop below is unrolled over the four stages, so
-    // every LDS address is a lane base plus an immediate; `st` is
-    // it % kStages, and the P parity it % 2 follows):
+    // Iteration `it` (unrolled over the four stages, so every LDS address is
+    // a lane base plus an immediate; `st` is it % kStages, and the P parity
+    // it % 2 follows):
     //   wait for tile it's rows; barrier A (tile it, P(it-1), the flags of
-    //   it-1; stage it-2 is free); gather tile it+2; settle the flags of
-    //   it-1 (owners move references, rewrite P(it-1), publish factors);
-    //   QK(it) -> partials; barrier B; then softmax(it) -> P(it) beside
-    //   P.V(it-1), which need no barrier between them.
-    auto step = [&](auto st, int it) {
+    //   it-1; stage it-2 is free); gather half of tile it+2; read the flags
+    //   of it-1; QK(it) -> partials; settle the flags (owners move
+    //   references, rewrite P(it-1), publish factors); barrier B; gather the
+    //   other half of tile it+2; then softmax(it) -> P(it) beside P.V(it-1),
+    //   which need no barrier between them.
+    // `kind` 0 is the first tile (no P.V, no flags), 1 a middle tile
+    // (1 <= it < n_tiles), 2 the final pass (it = n_tiles: P.V only); the
+    // middle tiles carry no tile-count tests around QK, softmax and P.V, so
+    // each phase is one basic block the compiler can interleave.
+    auto step = [&](auto st, auto kind_c, int it) {
       constexpr int S = decltype(st)::value;
+      constexpr int kind = decltype(kind_c)::value;
+      constexpr bool has_qk = kind != 2, has_pv = kind != 0;
       constexpr int SP = (S + kStages - 1) % kStages;  // tile it-1
       constexpr int SN = (S + 2) % kStages;            // tile it+2
       constexpr int PAR = S & 1, PARP = PAR ^ 1;      // P of tile it, of it-1
-      if (it < n_tiles) {
+      if constexpr (has_qk) {
         // this wave's rows of tile `it` landed (tile it+1 may still fly)
         if (it + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0F70 | kInstsPerWave);
         else __builtin_amdgcn_s_waitcnt(0x0F70);
       }
       __syncthreads();  // A
+      const bool more = it + 2 < n_tiles;
       uint32_t vm_after = 0u;
-      if (it + 2 < n_tiles) {
+      if (more) {
         // tile it+2 is the lookup's first tile when it is even, else its second
-        issue(lk, SN, S & 1);
+        issue(lk, SN, S & 1, 0, kInstsPerWave / 2);
         vm_after = static_cast<uint32_t>(lk.valid >> (32 * (S & 1)));
-        if ((S & 1) && it + 3 < n_tiles) lk = lookup(tile_lo + it + 3);
       }
       int any = 0;
-      if (it >= 1) {
-        // ---- flags of tile it-1: move the references where a tile max
-        // passed them by more than the slack (uniform decision)
+      if constexpr (has_pv) {
 #pragma unroll
         for (int w = 0; w < kNW; ++w) any |= s_flag[w];
+      }
+      f32x4_t s0, s1;
+      if constexpr (has_qk) qk(std::integral_constant<int, S>{}, s0, s1);
+      if constexpr (has_pv) {
+        // ---- flags of tile it-1: move the references where a tile max
+        // passed them by more than the slack (uniform decision)
         if (__builtin_expect(any, 0)) {
           const float tmax = fmaxf(s_mx[0][own_head], s_mx[1][own_head]);
           const bool bump = tmax > m_ref + kSlack;
@@ -349,22 +384,24 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
         }
         l_part += psum;
       }
-      f32x4_t s0, s1;
-      if (it < n_tiles) {
-        qk(std::integral_constant<int, S>{}, s0, s1);
-        // the partner owns the other head tile of these keys
-        *reinterpret_cast<f32x4_t*>(&xs[wave][lane * 4]) = dh ? s0 : s1;
-      }
+      // the partner owns the other head tile of these keys
+      if constexpr (has_qk) *reinterpret_cast<f32x4_t*>(&xs[wave][lane * 4]) = dh ? s0 : s1;
       __syncthreads();  // B: partials, P(it-1) as settled, the factors
-      if (__builtin_expect(any, 0)) {
+      if (more) {
+        issue(lk, SN, S & 1, kInstsPerWave / 2, kInstsPerWave);
+        if ((S & 1) && it + 3 < n_tiles) lk = lookup(tile_lo + it + 3);
+      }
+      if constexpr (has_pv) {
+        if (__builtin_expect(any, 0)) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const f32x4_t al = *reinterpret_cast<const f32x4_t*>(&s_alpha[16 * a + 4 * kb]);
+          for (int a = 0; a < 4; ++a) {
+            const f32x4_t al = *reinterpret_cast<const f32x4_t*>(&s_alpha[16 * a + 4 * kb]);
 #pragma unroll
-          for (int n = 0; n < 4; ++n) o[a][n] *= al;
+            for (int n = 0; n < 4; ++n) o[a][n] *= al;
+          }
         }
       }
-      if (it < n_tiles) {
+      if constexpr (has_qk) {
         // ---- softmax of the owned (head tile, key half): rows 4 kb + i are
         // keys 16 kh + 4 i + kb
         const f32x4_t mine = dh ? s1 : s0;
@@ -377,23 +414,39 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
           mx = fmaxf(mx, sv[i]);
         }
         mx = rows_max(mx);
-        if (kb == 0) s_mx[kh][own_head] = mx;
+        s_mx[kh][own_head] = mx;  // the four lanes of a head store the same value
         const bool flag = __ballot(mx > m_ref + kSlack) != 0;
-        if (lane == 0) s_flag[wave] = flag ? 1 : 0;
+        s_flag[wave] = flag ? 1 : 0;  // wave-uniform
         write_p(m_ref, std::integral_constant<int, PAR>{});
       }
-      if (it >= 1) pv(std::integral_constant<int, SP>{}, std::integral_constant<int, PARP>{});
+      if constexpr (has_pv) pv(std::integral_constant<int, SP>{}, std::integral_constant<int, PARP>{});
       vm_cur = vm_next;
       vm_next = vm_after;
     };
-    for (int it = 0; it <= n_tiles; it += kStages) {
-      step(std::integral_constant<int, 0>{}, it);
-      if (it + 1 > n_tiles) break;
-      step(std::integral_constant<int, 1>{}, it + 1);
-      if (it + 2 > n_tiles) break;
-      step(std::integral_constant<int, 2>{}, it + 2);
-      if (it + 3 > n_tiles) break;
-      step(std::integral_constant<int, 3>{}, it + 3);
+    using K0 = std::integral_constant<int, 0>;
+    using K1 = std::integral_constant<int, 1>;
+    using K2 = std::integral_constant<int, 2>;
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    step(S0{}, K0{}, 0);
+    int it = 1;
+    for (; it + kStages <= n_tiles; it += kStages) {
+      step(S1{}, K1{}, it);
+      step(S2{}, K1{}, it + 1);
+      step(S3{}, K1{}, it + 2);
+      step(S0{}, K1{}, it + 3);
+    }
+    // it % 4 == 1 here, and at most three middle tiles are left
+    if (it < n_tiles) step(S1{}, K1{}, it++);
+    if (it < n_tiles) step(S2{}, K1{}, it++);
+    if (it < n_tiles) step(S3{}, K1{}, it++);
+    switch (it & 3) {  // it == n_tiles: the last tile's P.V
+      case 0: step(S0{}, K2{}, it); break;
+      case 1: step(S1{}, K2{}, it); break;
+      case 2: step(S2{}, K2{}, it); break;
+      default: step(S3{}, K2{}, it); break;
     }
   }
 
@@ -449,7 +502,7 @@ bool dsv4_attn_h64_fits(int32_t topk) {
                              + sizeof(float) * kNW * 64 * 4           // xs
                              + sizeof(uint16_t) * 2 * kH * kPStride   // pbuf
                              + sizeof(float) * (2 * kH + kH + 2 * kH) // s_mx, s_alpha, s_l
-                             + sizeof(int) * (kNW + 1);               // s_flag, s_last
+                             + sizeof(int) * (2 * kNW);               // s_flag, s_lastw
   return kStatic + sizeof(int) * static_cast<size_t>(topk) <= 160 * 1024;
 }
 

@@ -108,6 +108,17 @@ __device__ __forceinline__ void global_to_lds16_s(const void* sbase, uint32_t vo
                : "memory");
 }
 
+// 4 bytes per lane (global_load_lds_dword): lane L of the wave writes
+// lds_wave_base + 4*L; lanes masked off by exec write nothing.
+__device__ __forceinline__ void global_to_lds4(const void* g, const void* lds_wave_base) {
+  const uint32_t lds = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_wave_base));
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
 // s_waitcnt immediates (gfx9 encoding): vmcnt(n) with the other counters open,
 // and lgkmcnt(0) with the others open.
 constexpr int kWaitVm0 = 0x0F70;
