@@ -8,23 +8,18 @@
 //
 // Same definition, arguments and key walk as sparse_attn_kernel (one
 // workgroup per query, 32-key tiles gathered straight into LDS, key slots
-// masked from positions), with a work split chosen for LDS traffic, which
-// bounds the per-head-group layout at this shape: each K element read from
-// LDS there feeds 16 heads, and the transposed V reads (ds_read_b64_tr_b16)
-// move half the bytes per clock of ds_read_b128.  Here, with 8 waves:
-//   * QK^T: wave w = hg + 2 dh + 4 kh computes partial scores S^T (16 keys x
-//     32 heads) for key half kh, head group hg (32 heads), over dim half dh
-//     (256 dims) -- its Q block (32 heads x 256 dims, 64 VGPRs) stays in
-//     registers, and every K fragment read feeds two MFMAs (32 heads);
-//   * the partials of head tile (hg, 1 - dh) go through LDS to the wave that
-//     owns that tile, which adds its own: each (head tile, key half) has one
-//     owner, which runs the online softmax for it and writes P (bf16) to an
-//     LDS tile [head][key];
+// masked from positions), with a work split chosen for this shape.  With 8
+// waves:
+//   * QK^T: wave w = hq + 4 kh computes S^T (16 keys x 16 heads) for key half
+//     kh and head tile hq over all 512 dims -- its Q block (16 heads x 512
+//     dims, 64 VGPRs) stays in registers, so the scores need no exchange
+//     between waves; the wave then owns that (head tile, key half) for the
+//     online softmax and writes P (bf16) to an LDS tile [head][key];
 //   * P.V: wave w accumulates O for all 64 heads x dims 64w .. 64w+63
-//     (64 VGPRs): every transposed V read feeds four MFMAs (64 heads);
-//   * per 32-key tile, each CU then reads 64 KiB of K, 32 KiB of V, 8 KiB of
-//     partial scores and 32 KiB of P from LDS, against 128 + 128 + 32 KiB
-//     in the per-head-group layout.
+//     (64 VGPRs): every transposed V read (ds_read_b64_tr_b16, half the bytes
+//     per clock of ds_read_b128) feeds four MFMAs (64 heads);
+//   * per 32-key tile, each CU reads 128 KiB of K, 32 KiB of V and 32 KiB of
+//     P from LDS.
 // Softmax: online, fp32, exp2 with the scale folded in, against a per-head
 // reference max that moves lazily.  Each owner computes P against the
 // current reference and flags its heads whose tile max passes it by more
@@ -32,10 +27,10 @@
 // (the first tile of every query, and rare jumps) do the owners move the
 // reference, rewrite that tile's P and publish the rescale factors, which
 // costs one more barrier.  Otherwise p <= 2^8.
-// Pipeline, two barriers per tile (three LDS stages): iteration t waits for
-// tile t's gather, barrier A (publishes tile t, P(t-1), the flags), checks
-// the flags of t-1, P.V(t-1), QK(t), barrier B (publishes the partials;
-// stage t-1 is free), gathers tile t+2, softmax(t) -> P(t).
+// Pipeline, one barrier per tile over four LDS stages: P, the tile maxima
+// and the flags are double-buffered by tile parity, so after the barrier of
+// tile t a wave runs P.V(t-1), QK(t) and softmax(t) with no barrier between
+// them, while the gathers of tiles t+1 and t+2 are in flight.
 #include <type_traits>
 
 #include "dsv4_device.h"
@@ -84,12 +79,14 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
                 const int32_t* __restrict__ sel, int topk, uint16_t* __restrict__ out,
                 int nsplit, float* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(16))) uint16_t tiles[kStages][kTileElems];
-  __shared__ __attribute__((aligned(16))) float xs[kNW][64 * 4];   // partial scores for the partner
-  __shared__ __attribute__((aligned(16))) uint16_t pbuf[2][kH * kPStride];  // P, by tile parity
-  __shared__ float s_mx[2][kH];      // per key half: the owner's tile max (log2 units)
+  // P of even and of odd tiles: two arrays, so the compiler knows that the
+  // P.V reads of one never alias the softmax's stores to the other
+  __shared__ __attribute__((aligned(16))) uint16_t pbuf0[kH * kPStride];
+  __shared__ __attribute__((aligned(16))) uint16_t pbuf1[kH * kPStride];
+  __shared__ float s_mx[2][2][kH];   // by tile parity, per key half: the tile max (log2 units)
   __shared__ __attribute__((aligned(16))) float s_alpha[kH];  // rescale factors of a flagged tile
   __shared__ float s_l[2][kH];       // per key half: the owner's row sum
-  __shared__ int s_flag[kNW];
+  __shared__ int s_flag[2][kNW];     // by tile parity
   __shared__ int s_lastw[kNW];  // per wave: its last visible selection slot
   extern __shared__ int s_sel[];     // the query's selection row (topk ints)
 
@@ -99,11 +96,9 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
   const int kb = lane >> 4;
   const int l16 = lane & 15;
   // QK / softmax role
-  const int hg = wave & 1;         // head group: heads 32 hg .. 32 hg + 31
-  const int dh = (wave >> 1) & 1;  // dim half of the partial scores; owned head tile
+  const int hq = wave & 3;         // head tile: heads 16 hq .. 16 hq + 15
   const int kh = wave >> 2;        // key half of the tile: keys 16 kh .. 16 kh + 15
-  const int partner = wave ^ 2;    // same heads and keys, other dim half
-  const int own_head = 32 * hg + 16 * dh + l16;
+  const int own_head = 16 * hq + l16;
   // P.V role: dims 64 wave .. 64 wave + 63 of all heads
 
   int64_t t;
@@ -120,16 +115,13 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
   const uint16_t* self_row = raw + (p - raw_pos0) * kD;
 
   // ---- Q block: B operand of S^T = K.Q^T.  Lane group kb holds dims
-  // 256 dh + 64 kb .. + 63 over the 8 steps (the contraction order is the
+  // 128 kb .. 128 kb + 127 over the 16 steps (the contraction order is the
   // same permutation for K below).
-  bf16x8_t qf[2][8];
+  bf16x8_t qf[16];
   {
+    const uint16_t* qp = q + ((t * kH + own_head) * (int64_t)kD + 128 * kb);
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      const uint16_t* qp = q + ((t * kH + 32 * hg + 16 * ht + l16) * (int64_t)kD + 256 * dh + 64 * kb);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qf[ht][j] = *reinterpret_cast<const bf16x8_t*>(qp + 8 * j);
-    }
+    for (int j = 0; j < 16; ++j) qf[j] = *reinterpret_cast<const bf16x8_t*>(qp + 8 * j);
   }
 
   int n_slots;
@@ -246,35 +238,22 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
     asm volatile("" : "+v"(x));
     return x;
   };
-  auto qk = [&](auto stage, f32x4_t& s0, f32x4_t& s1) {
+  auto qk = [&](auto stage) -> f32x4_t {
     const uint16_t* rb = tiles[decltype(stage)::value] + qk_row * kD;
     const int q_swz = opaque(qk_swz);
-    s0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    bf16x8_t fa[2][2];
-    auto ld = [&](int j0, int bi) {
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int chunk = 32 * dh + 8 * kb + j0 + u;
-        fa[bi][u] = *reinterpret_cast<const bf16x8_t*>(rb + ((chunk ^ q_swz) * 8));
-      }
-    };
-    ld(0, 0);
-#pragma unroll
-    for (int j0 = 0; j0 < 8; j0 += 2) {
-      const int bi = (j0 >> 1) & 1;
-      if (j0 + 2 < 8) ld(j0 + 2, bi ^ 1);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[bi][u], qf[0][j0 + u], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[bi][u], qf[1][j0 + u], s1, 0, 0, 0);
-      }
+    for (int j = 0; j < 16; ++j) {
+      const int chunk = 16 * kb + j;
+      const bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(rb + ((chunk ^ q_swz) * 8));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, qf[j], acc, 0, 0, 0);
     }
+    return acc;
   };
 
   auto pv = [&](auto stage, auto par) {
     const uint16_t* tb = tiles[decltype(stage)::value];
-    const uint16_t* pb = pbuf[decltype(par)::value];
+    const uint16_t* pb = decltype(par)::value ? pbuf1 : pbuf0;
     const int s0w = opaque(sw0), s1w = opaque(sw1);
     bf16x8_t pa[4];
 #pragma unroll
@@ -314,7 +293,8 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
     uint2 w;
     w.x = pack_bf16x2(pr[0], pr[1]);
     w.y = pack_bf16x2(pr[2], pr[3]);
-    *reinterpret_cast<uint2*>(&pbuf[decltype(par)::value][own_head * kPStride + 8 * kb + 4 * kh]) = w;
+    uint16_t* pw = decltype(par)::value ? pbuf1 : pbuf0;
+    *reinterpret_cast<uint2*>(&pw[own_head * kPStride + 8 * kb + 4 * kh]) = w;
     psum = rows_sum(s);
   };
 
@@ -328,50 +308,46 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
     }
     if (n_tiles > 2) lk = lookup(tile_lo + 2);  // tiles 2 and 3
     // Iteration `it` (unrolled over the four stages, so every LDS address is
-    // a lane base plus an immediate; `st` is it % kStages, and the P parity
-    // it % 2 follows):
-    //   wait for tile it's rows; barrier A (tile it, P(it-1), the flags of
-    //   it-1; stage it-2 is free); gather half of tile it+2; read the flags
-    //   of it-1; QK(it) -> partials; settle the flags (owners move
-    //   references, rewrite P(it-1), publish factors); barrier B; gather the
-    //   other half of tile it+2; then softmax(it) -> P(it) beside P.V(it-1),
-    //   which need no barrier between them.
+    // a lane base plus an immediate; `st` is it % kStages, and the parity
+    // it % 2 of P, the tile maxima and the flags follows):
+    //   wait for tile it's rows; the barrier (tile it, P(it-1), the maxima
+    //   and flags of it-1; stage it-2 and the parity-it buffers are free);
+    //   gather tile it+2; settle the flags of it-1 (owners move references,
+    //   rewrite P(it-1), publish factors; one more barrier, rare); then
+    //   P.V(it-1), QK(it) and softmax(it) -> P(it), which need no barrier
+    //   between them.
     // `kind` 0 is the first tile (no P.V, no flags), 1 a middle tile
     // (1 <= it < n_tiles), 2 the final pass (it = n_tiles: P.V only); the
-    // middle tiles carry no tile-count tests around QK, softmax and P.V, so
-    // each phase is one basic block the compiler can interleave.
+    // middle tiles carry no tile-count tests around P.V, QK and softmax, so
+    // those are one basic block the compiler can interleave.
     auto step = [&](auto st, auto kind_c, int it) {
       constexpr int S = decltype(st)::value;
       constexpr int kind = decltype(kind_c)::value;
       constexpr bool has_qk = kind != 2, has_pv = kind != 0;
       constexpr int SP = (S + kStages - 1) % kStages;  // tile it-1
       constexpr int SN = (S + 2) % kStages;            // tile it+2
-      constexpr int PAR = S & 1, PARP = PAR ^ 1;      // P of tile it, of it-1
+      constexpr int PAR = S & 1, PARP = PAR ^ 1;      // parity of tile it, of it-1
       if constexpr (has_qk) {
         // this wave's rows of tile `it` landed (tile it+1 may still fly)
         if (it + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0F70 | kInstsPerWave);
         else __builtin_amdgcn_s_waitcnt(0x0F70);
       }
-      __syncthreads();  // A
-      const bool more = it + 2 < n_tiles;
+      __syncthreads();
       uint32_t vm_after = 0u;
-      if (more) {
+      if (it + 2 < n_tiles) {
         // tile it+2 is the lookup's first tile when it is even, else its second
-        issue(lk, SN, S & 1, 0, kInstsPerWave / 2);
+        issue(lk, SN, S & 1, 0, kInstsPerWave);
         vm_after = static_cast<uint32_t>(lk.valid >> (32 * (S & 1)));
+        if ((S & 1) && it + 3 < n_tiles) lk = lookup(tile_lo + it + 3);
       }
-      int any = 0;
-      if constexpr (has_pv) {
-#pragma unroll
-        for (int w = 0; w < kNW; ++w) any |= s_flag[w];
-      }
-      f32x4_t s0, s1;
-      if constexpr (has_qk) qk(std::integral_constant<int, S>{}, s0, s1);
       if constexpr (has_pv) {
         // ---- flags of tile it-1: move the references where a tile max
         // passed them by more than the slack (uniform decision)
+        int any = 0;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) any |= s_flag[PARP][w];
         if (__builtin_expect(any, 0)) {
-          const float tmax = fmaxf(s_mx[0][own_head], s_mx[1][own_head]);
+          const float tmax = fmaxf(s_mx[PARP][0][own_head], s_mx[PARP][1][own_head]);
           const bool bump = tmax > m_ref + kSlack;
           const float m_new = bump ? tmax : m_ref;
           const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -381,18 +357,7 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
           psum = l_part * alpha + psum;
           l_part = 0.f;
           m_ref = m_new;
-        }
-        l_part += psum;
-      }
-      // the partner owns the other head tile of these keys
-      if constexpr (has_qk) *reinterpret_cast<f32x4_t*>(&xs[wave][lane * 4]) = dh ? s0 : s1;
-      __syncthreads();  // B: partials, P(it-1) as settled, the factors
-      if (more) {
-        issue(lk, SN, S & 1, kInstsPerWave / 2, kInstsPerWave);
-        if ((S & 1) && it + 3 < n_tiles) lk = lookup(tile_lo + it + 3);
-      }
-      if constexpr (has_pv) {
-        if (__builtin_expect(any, 0)) {
+          __syncthreads();  // P(it-1) as settled, the factors
 #pragma unroll
           for (int a = 0; a < 4; ++a) {
             const f32x4_t al = *reinterpret_cast<const f32x4_t*>(&s_alpha[16 * a + 4 * kb]);
@@ -400,26 +365,26 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
             for (int n = 0; n < 4; ++n) o[a][n] *= al;
           }
         }
+        l_part += psum;
+        pv(std::integral_constant<int, SP>{}, std::integral_constant<int, PARP>{});
       }
       if constexpr (has_qk) {
-        // ---- softmax of the owned (head tile, key half): rows 4 kb + i are
-        // keys 16 kh + 4 i + kb
-        const f32x4_t mine = dh ? s1 : s0;
-        const f32x4_t other = *reinterpret_cast<const f32x4_t*>(&xs[partner][lane * 4]);
+        // ---- QK(it) and the softmax of the owned (head tile, key half):
+        // rows 4 kb + i are keys 16 kh + 4 i + kb
+        const f32x4_t sc = qk(std::integral_constant<int, S>{});
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = 16 * kh + 4 * i + kb;
-          sv[i] = ((vm_cur >> key) & 1u) ? (mine[i] + other[i]) * scale_log2 : -INFINITY;
+          sv[i] = ((vm_cur >> key) & 1u) ? sc[i] * scale_log2 : -INFINITY;
           mx = fmaxf(mx, sv[i]);
         }
         mx = rows_max(mx);
-        s_mx[kh][own_head] = mx;  // the four lanes of a head store the same value
+        s_mx[PAR][kh][own_head] = mx;  // the four lanes of a head store the same value
         const bool flag = __ballot(mx > m_ref + kSlack) != 0;
-        s_flag[wave] = flag ? 1 : 0;  // wave-uniform
+        s_flag[PAR][wave] = flag ? 1 : 0;  // wave-uniform
         write_p(m_ref, std::integral_constant<int, PAR>{});
       }
-      if constexpr (has_pv) pv(std::integral_constant<int, SP>{}, std::integral_constant<int, PARP>{});
       vm_cur = vm_next;
       vm_next = vm_after;
     };
@@ -496,13 +461,12 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
 }  // namespace
 
 // Whether the kernel's LDS (static arrays + the selection row, topk ints)
-// fits a workgroup's 160 KiB: up to k = 3,255 selected slots.
+// fits a workgroup's 160 KiB: up to k = 5,160 selected slots.
 bool dsv4_attn_h64_fits(int32_t topk) {
   constexpr size_t kStatic = sizeof(uint16_t) * kStages * kTileElems   // tiles
-                             + sizeof(float) * kNW * 64 * 4           // xs
-                             + sizeof(uint16_t) * 2 * kH * kPStride   // pbuf
-                             + sizeof(float) * (2 * kH + kH + 2 * kH) // s_mx, s_alpha, s_l
-                             + sizeof(int) * (2 * kNW);               // s_flag, s_lastw
+                             + sizeof(uint16_t) * 2 * kH * kPStride   // pbuf0, pbuf1
+                             + sizeof(float) * (4 * kH + kH + 2 * kH) // s_mx, s_alpha, s_l
+                             + sizeof(int) * (3 * kNW);               // s_flag, s_lastw
   return kStatic + sizeof(int) * static_cast<size_t>(topk) <= 160 * 1024;
 }
 

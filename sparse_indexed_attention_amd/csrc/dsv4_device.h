@@ -165,7 +165,7 @@ hipError_t dsv4_launch_sparse_attn(const void* q, int64_t T, int64_t q_pos0, int
                                    void* out, int32_t nsplit, float* part_o, float* part_ml,
                                    hipStream_t s);
 // The H = 64, D = 512 kernel (attn_h64.hip); scale_log2 = scale * log2(e).
-// It takes selections of at most 3,255 slots (its LDS holds the row).
+// It takes selections of at most 5,160 slots (its LDS holds the row).
 bool dsv4_attn_h64_fits(int32_t topk);
 hipError_t dsv4_launch_sparse_attn_h64(const void* q, int64_t T, int64_t q_pos0, float scale_log2,
                                        const void* raw_kv, int64_t raw_pos0, int32_t window,
