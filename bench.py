@@ -258,7 +258,7 @@ def parse():
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DB", "BENCH_LOG", "OUT_MD"),
                     help="write the kernel-trace summary of a profiled bench run and exit")
     ap.add_argument("--commands", default="",
-                    help="text of the commands, for --summarize-pmc / --summarize-trace")
+                    help="text of the commands, for --summarize-counters / --summarize-trace")
     return ap.parse_args()
 
 
