@@ -259,6 +259,11 @@ def parse():
                     help="write the kernel-trace summary of a profiled bench run and exit")
     ap.add_argument("--commands", default="",
                     help="text of the commands, for --summarize-counters / --summarize-trace")
+    ap.add_argument("--ab", nargs=2, metavar=("LIB_A", "LIB_B"),
+                    help="instead of the benchmark, time one operation of two builds of the "
+                         "library in this process, alternating rounds (see ab_compare)")
+    ap.add_argument("--ab-op", default="attention", choices=("attention", "select", "score", "topk"))
+    ap.add_argument("--ab-rounds", type=int, default=8)
     return ap.parse_args()
 
 
@@ -662,6 +667,90 @@ def summarize_trace(db: str, log: str, out_md: str, cmds: str):
     print(open(out_md).read())
 
 
+def engine_clocks_mhz() -> list:
+    """Current shader clock of each GPU the host's sysfs lists (the line the
+    driver marks with '*' in pp_dpm_sclk), where readable; else empty."""
+    import glob
+    out = []
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(f):
+                if "*" in line:
+                    out.append(int("".join(ch for ch in line.split(":")[1] if ch.isdigit())))
+        except (OSError, ValueError, IndexError):
+            pass
+    return out
+
+
+def ab_compare(args, wl: SI.Workload) -> dict:
+    """One operation of two library builds, A and B, in one process: both are
+    loaded side by side and called alternately on the same inputs (the chunk
+    state of the benchmark, prepared with A), `rounds` rounds of `reps` calls
+    each per build, HIP events around each round.  Reports per build the
+    median, min and max of the round means, and B / A of the medians; the
+    engine clock read from sysfs before and after each round where the host
+    exposes it."""
+    import sparse_indexed_attention_amd as dsv4
+    la = dsv4.use_library(os.path.abspath(args.ab[0]))
+    lb = dsv4._load(os.path.abspath(args.ab[1]))
+    dsv4.use_library(la)
+    st = Setup(wl, args.seed)
+    st.step()
+    torch.cuda.synchronize()
+    d, T = dsv4, wl.chunk
+    S = st.S_after
+    stride = d.dsv4_score_stride(S)
+    sc = st.scratch[:st.tile * stride].view(st.tile, stride)
+    t0 = T - st.tile
+    if args.ab_op == "topk":
+        # the scores of the last query tile, then the top-k the select runs
+        # on them (as in the benchmark: the two-pass kernel with a workspace
+        # over rows longer than one chunk, so the scores stay intact)
+        d.dsv4_indexer_scores(st.icache, st.q_idx[t0:], st.w[t0:], wl.q_pos0 + t0, sc, True)
+        torch.cuda.synchronize()
+        split_ws = d.dsv4_topk_split_workspace_bytes(st.tile, wl.q_pos0 + t0, wl.topk)
+        ws_t = torch.empty(max(1, split_ws // 4), dtype=torch.float32, device="cuda")
+    ops = {
+        "attention": lambda: d.dsv4_sparse_prefill_attn(st.q_attn, wl.q_pos0, st.raw_kv,
+                                                        st.raw_pos0, wl.window, st.acache,
+                                                        st.idx, st.out),
+        "select": lambda: d.dsv4_indexer_select(st.icache, st.acache.n_rows, st.q_idx, st.w,
+                                                wl.chunk, wl.q_pos0, wl.idx_heads, wl.topk,
+                                                st.idx, st.scratch, wl.tile_rows),
+        "score": lambda: d.dsv4_indexer_scores(st.icache, st.q_idx[t0:], st.w[t0:],
+                                               wl.q_pos0 + t0, sc, True),
+        "topk": (lambda: d.dsv4_topk_select_split(sc, wl.q_pos0 + t0, S, wl.topk, st.idx[t0:], ws_t))
+        if args.ab_op == "topk" and split_ws > 0 else
+        (lambda: d.dsv4_topk_select(sc, wl.q_pos0 + t0, S, wl.topk, st.idx[t0:])),
+    }
+    fn = ops[args.ab_op]
+    reps = max(10, args.steps)
+    times = {"A": [], "B": []}
+    clocks = {"A": [], "B": []}
+    for name, L in (("A", la), ("B", lb)):  # warm both
+        d.use_library(L)
+        for _ in range(reps):
+            fn()
+    torch.cuda.synchronize()
+    for r in range(args.ab_rounds):
+        order = (("A", la), ("B", lb)) if r % 2 == 0 else (("B", lb), ("A", la))
+        for name, L in order:
+            d.use_library(L)
+            c0 = engine_clocks_mhz()
+            times[name].append(timed_kernel(fn, reps))
+            clocks[name].append([c0, engine_clocks_mhz()])
+    d.use_library(la)
+    summ = {}
+    for name in ("A", "B"):
+        v = np.array(times[name])
+        summ[name] = {"lib": args.ab[0 if name == "A" else 1], "median_ms": float(np.median(v)),
+                      "min_ms": float(v.min()), "max_ms": float(v.max()),
+                      "rounds_ms": [round(float(x), 4) for x in v], "clock_mhz": clocks[name]}
+    return {"ab": args.ab_op, "workload": wl.name, "rounds": args.ab_rounds, "calls_per_round": reps,
+            "A": summ["A"], "B": summ["B"],
+            "B_over_A": summ["B"]["median_ms"] / summ["A"]["median_ms"]}
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -676,6 +765,9 @@ def main():
               "has no multi-GPU path (see the sharding note in the design notes).", file=sys.stderr)
         sys.exit(2)
     torch.cuda.init()
+    if args.ab:
+        print(json.dumps(ab_compare(args, SI.WORKLOADS[args.workload])))
+        return
     if args.matrix:
         tile_matrix(max(3, args.steps // 4))
         return

@@ -20,7 +20,7 @@ __all__ = [
     "dsv4_indexer_scratch_bytes", "dsv4_compress", "dsv4_indexer_scores", "dsv4_topk_select",
     "dsv4_indexer_select", "dsv4_sparse_prefill_attn", "dsv4_sparse_attn_narrow_plan",
     "dsv4_sparse_attn_narrow", "dsv4_topk_split_workspace_bytes", "dsv4_topk_select_split",
-    "dsv4_indexer_select_noalloc", "DSV4_NOALLOC_SCRATCH_BYTES",
+    "dsv4_indexer_select_noalloc", "DSV4_NOALLOC_SCRATCH_BYTES", "use_library",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -78,19 +78,33 @@ _SIGNATURES = {
 _lib = None
 
 
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m sparse_indexed_attention_amd.build`")
+    L = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
 def lib() -> ctypes.CDLL:
     """Load libdsv4.so (built by ``python -m sparse_indexed_attention_amd.build``)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with "
-                              "`python -m sparse_indexed_attention_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in _SIGNATURES.items():
-            fn = getattr(L, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = L
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+def use_library(path_or_handle) -> ctypes.CDLL:
+    """Make the functions below call another build of the library (a path,
+    or a handle this function returned before); returns the handle now in
+    use.  Two builds can be loaded side by side, e.g. for an interleaved
+    timing comparison in one process."""
+    global _lib
+    _lib = path_or_handle if isinstance(path_or_handle, ctypes.CDLL) else _load(path_or_handle)
     return _lib
 
 
