@@ -22,6 +22,23 @@ def test_library_exports_every_header_function():
     assert set(names) == set(dsv4._SIGNATURES)
 
 
+def test_use_library_switches_and_restores():
+    # a second handle on the same build, then back to the first by handle
+    first = dsv4.lib()
+    second = dsv4.use_library(dsv4.LIB_PATH)
+    try:
+        assert second is not first
+        assert dsv4.lib() is second
+        assert second.dsv4_abi_version() == first.dsv4_abi_version()
+        assert dsv4.dsv4_score_stride(1000) == first.dsv4_score_stride(1000)
+    finally:
+        assert dsv4.use_library(first) is first
+    assert dsv4.lib() is first
+    with pytest.raises(ImportError):
+        dsv4.use_library("/nonexistent/libdsv4.so")
+    assert dsv4.lib() is first
+
+
 def test_abi_version_and_host_helpers():
     assert dsv4.dsv4_abi_version() == 5
     assert dsv4.dsv4_indexer_all_pooled(0, 8) is False
