@@ -24,6 +24,8 @@
  *   - Every argument check runs on the host before anything is enqueued.  On
  *     a non-zero return nothing was enqueued, no host struct changed, and
  *     dsv4_last_error() describes the failure (thread-local string).
+ *   - Positions, counts, sizes and strides are at most DSV4_MAX_EXTENT;
+ *     byte sizes that would not fit a size_t are INVALID_ARG as well.
  *   - The kernels only implement the standard masks (causal window, pooled-row
  *     visibility rebuilt from positions [P2 commit 1]); they never take a mask
  *     tensor.  A caller needing another mask must use its own path.
@@ -45,8 +47,10 @@ extern "C" {
 
 /* 4: dsv4_indexer_select may keep top-k candidates in its scratch (the
  * scores are not left there), and dsv4_topk_select_split takes more rows.
- * 5: dsv4_indexer_select_noalloc. */
-#define DSV4_ABI_VERSION 5
+ * 5: dsv4_indexer_select_noalloc.
+ * 6: extents above DSV4_MAX_EXTENT are rejected; dsv4_score_stride returns -1
+ * for them. */
+#define DSV4_ABI_VERSION 6
 
 /* Return codes. */
 #define DSV4_OK                0
@@ -72,6 +76,11 @@ extern "C" {
 #define DSV4_MAX_ATTN_SPLITS 64
 /* Bytes of the per-GPU static score scratch of dsv4_indexer_select_noalloc. */
 #define DSV4_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+/* Largest position, count, size or stride any entry point takes (a cache's
+ * capacity and n_rows included): 2^40, far past any real context, so that the
+ * host's index and size arithmetic cannot overflow.  Larger values are
+ * INVALID_ARG. */
+#define DSV4_MAX_EXTENT ((int64_t)1 << 40)
 
 /*
  * PoolingCache of one compressor [P1 Summary, Correctness; P2 commit 4].
@@ -118,7 +127,8 @@ int dsv4_indexer_all_pooled(int64_t n_rows, int32_t topk);
 
 /*
  * Row stride, in floats, of the score scratch for a cache holding n_rows
- * pooled rows (n_rows rounded up to a multiple of 64).
+ * pooled rows (n_rows rounded up to a multiple of 64; 64 for n_rows <= 0;
+ * -1 for n_rows above DSV4_MAX_EXTENT).
  */
 int64_t dsv4_score_stride(int64_t n_rows);
 

@@ -52,6 +52,14 @@ int dsv4_internal_fail(int code, const char* fmt, ...) {
 
 namespace {
 
+// Positions, counts, sizes and strides the entry points take: 0 ..
+// DSV4_MAX_EXTENT (2^40), so sums of a few of them, and their products with
+// the small factors below, stay inside int64_t.
+inline bool extent_ok(int64_t v) { return v >= 0 && v <= DSV4_MAX_EXTENT; }
+
+// a * b into *out; false when the product does not fit a size_t.
+inline bool mul_size(size_t a, size_t b, size_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
 // Pool ratios accepted by the compressor and the attention: 4 (indexer and
 // sparse attention) and 128 (CompressedAttention) are the pages'; any ratio
 // in [2, DSV4_MAX_RATIO] follows the same definitions.  The indexer entry
@@ -66,7 +74,7 @@ int check_cache(const dsv4_pool_cache* c, const char* name, int need_ratio = 0) 
   if (c->dtype != DSV4_BF16 && c->dtype != DSV4_F32)
     return fail(DSV4_ERR_UNSUPPORTED, "%s: dtype %d", name, c->dtype);
   if (c->dim <= 0) return fail(DSV4_ERR_INVALID_ARG, "%s: dim %d", name, c->dim);
-  if (c->capacity < 0 || c->n_rows < 0 || c->n_rows > c->capacity)
+  if (!extent_ok(c->capacity) || c->n_rows < 0 || c->n_rows > c->capacity)
     return fail(DSV4_ERR_INVALID_ARG, "%s: n_rows %lld / capacity %lld", name,
                 (long long)c->n_rows, (long long)c->capacity);
   if (c->n_rem < 0 || c->n_rem >= c->ratio)
@@ -115,24 +123,31 @@ int dsv4_indexer_all_pooled(int64_t n_rows, int32_t topk) {
 
 int64_t dsv4_score_stride(int64_t n_rows) {
   if (n_rows <= 0) return 64;
+  if (n_rows > DSV4_MAX_EXTENT) return -1;
   return (n_rows + 63) / 64 * 64;
 }
 
 int dsv4_indexer_scratch_bytes(int64_t tile_rows, int64_t max_rows, size_t* bytes) {
-  if (!bytes || tile_rows < 0 || max_rows < 0)
+  if (!bytes || !extent_ok(tile_rows) || !extent_ok(max_rows))
     return fail(DSV4_ERR_INVALID_ARG, "scratch_bytes: bad arguments");
-  *bytes = static_cast<size_t>(tile_rows) * static_cast<size_t>(dsv4_score_stride(max_rows)) *
-           sizeof(float);
+  size_t n = 0;
+  if (!mul_size(static_cast<size_t>(tile_rows),
+                static_cast<size_t>(dsv4_score_stride(max_rows)) * sizeof(float), &n))
+    return fail(DSV4_ERR_INVALID_ARG, "scratch_bytes: %lld x %lld scores overflow size_t",
+                (long long)tile_rows, (long long)max_rows);
   // narrow tiles over long rows: room for the chunk-parallel top-k as well
+  // (at most 64 x 2^25 chunks x DSV4_MAX_TOPK x 8 bytes: no overflow)
   if (tile_rows > 0 && tile_rows <= kSplitRows && max_rows > kTopkChunk)
-    *bytes += split_ws_bytes(tile_rows, (max_rows + kTopkChunk - 1) / kTopkChunk, DSV4_MAX_TOPK);
+    n += split_ws_bytes(tile_rows, (max_rows + kTopkChunk - 1) / kTopkChunk, DSV4_MAX_TOPK);
+  *bytes = n;
   return DSV4_OK;
 }
 
 int dsv4_compress(dsv4_pool_cache* cache, const void* x, int64_t n_new, void* stream) {
   int rc = check_cache(cache, "compress");
   if (rc) return rc;
-  if (n_new < 0) return fail(DSV4_ERR_INVALID_ARG, "compress: n_new %lld", (long long)n_new);
+  if (!extent_ok(n_new))
+    return fail(DSV4_ERR_INVALID_ARG, "compress: n_new %lld", (long long)n_new);
   if (n_new > 0 && !x) return fail(DSV4_ERR_INVALID_ARG, "compress: NULL input");
   const int64_t L = cache->n_rem + n_new;
   const int64_t groups = L / cache->ratio;
@@ -159,7 +174,9 @@ static int check_scores_args(const dsv4_pool_cache* ic, const void* q, const flo
     return fail(DSV4_ERR_UNSUPPORTED, "%s: index dim %d not in {32,64,128}", who, ic->dim);
   if (n_heads < 1 || n_heads > DSV4_MAX_INDEX_HEADS)
     return fail(DSV4_ERR_UNSUPPORTED, "%s: %d indexer heads", who, n_heads);
-  if (rows < 0 || q_pos0 < 0) return fail(DSV4_ERR_INVALID_ARG, "%s: rows/q_pos0 negative", who);
+  if (!extent_ok(rows) || !extent_ok(q_pos0))
+    return fail(DSV4_ERR_INVALID_ARG, "%s: rows %lld / q_pos0 %lld", who, (long long)rows,
+                (long long)q_pos0);
   if (rows > 0 && (!q || !w)) return fail(DSV4_ERR_INVALID_ARG, "%s: NULL q or w", who);
   if (rows > 0 && (!aligned16(q) || !aligned16(ic->rows)))
     return fail(DSV4_ERR_INVALID_ARG, "%s: q and cache rows must be 16-byte aligned", who);
@@ -195,7 +212,8 @@ int dsv4_indexer_scores(const dsv4_pool_cache* index_cache, const void* q, const
 static int check_topk_args(const char* who, const float* scores, int64_t rows, int64_t stride,
                            int64_t q_pos0, int64_t n_cols, int32_t topk,
                            const int32_t* out_idx) {
-  if (rows < 0 || q_pos0 < 0 || n_cols < 0 || stride < n_cols)
+  if (!extent_ok(rows) || !extent_ok(q_pos0) || !extent_ok(n_cols) || !extent_ok(stride) ||
+      stride < n_cols)
     return fail(DSV4_ERR_INVALID_ARG, "%s: bad sizes", who);
   if (topk < 1 || topk > DSV4_MAX_TOPK)
     return fail(DSV4_ERR_UNSUPPORTED, "%s: topk %d", who, topk);
@@ -218,7 +236,7 @@ int dsv4_topk_select(const float* scores, int64_t rows, int64_t stride, int64_t 
 }
 
 int dsv4_topk_split_workspace_bytes(int64_t rows, int64_t q_pos0, int32_t topk, size_t* bytes) {
-  if (!bytes || rows < 0 || q_pos0 < 0 || topk < 1 || topk > DSV4_MAX_TOPK)
+  if (!bytes || !extent_ok(rows) || !extent_ok(q_pos0) || topk < 1 || topk > DSV4_MAX_TOPK)
     return fail(DSV4_ERR_INVALID_ARG, "topk_split_workspace_bytes: bad arguments");
   *bytes = split_applies(rows, q_pos0, topk)
                ? split_ws_bytes(rows, dsv4_topk_split_chunks(rows, q_pos0), topk)
@@ -269,8 +287,9 @@ int dsv4_indexer_select(const dsv4_pool_cache* index_cache, int64_t n_attn_rows,
     return fail(DSV4_ERR_ROW_MISMATCH,
                 "indexer_select: index cache has %lld pooled rows, attention cache %lld",
                 (long long)S, (long long)n_attn_rows);
-  if (T < 0 || q_pos0 < 0 || tile_rows < 0)
-    return fail(DSV4_ERR_INVALID_ARG, "indexer_select: negative size");
+  if (!extent_ok(T) || !extent_ok(q_pos0) || tile_rows < 0)
+    return fail(DSV4_ERR_INVALID_ARG, "indexer_select: T %lld / q_pos0 %lld / tile_rows %d",
+                (long long)T, (long long)q_pos0, tile_rows);
   if (topk < 1 || topk > DSV4_MAX_TOPK)
     return fail(DSV4_ERR_UNSUPPORTED, "indexer_select: topk %d", topk);
   if (T > 0 && !out_idx) return fail(DSV4_ERR_INVALID_ARG, "indexer_select: NULL out_idx");
@@ -360,8 +379,8 @@ static int check_attn_args(const char* who, const void* q, int64_t T, int64_t q_
   if (n_heads < 1 || n_heads > DSV4_MAX_HEADS)
     return fail(DSV4_ERR_UNSUPPORTED, "%s: %d heads", who, n_heads);
   if (window < 1) return fail(DSV4_ERR_INVALID_ARG, "%s: window %d", who, window);
-  if (T < 0 || q_pos0 < 0 || raw_pos0 < 0 || n_raw < 0)
-    return fail(DSV4_ERR_INVALID_ARG, "%s: negative size", who);
+  if (!extent_ok(T) || !extent_ok(q_pos0) || !extent_ok(raw_pos0) || !extent_ok(n_raw))
+    return fail(DSV4_ERR_INVALID_ARG, "%s: size or position outside [0, 2^40]", who);
   if (sel_idx && (topk < 1 || topk > DSV4_MAX_TOPK))
     return fail(DSV4_ERR_UNSUPPORTED, "%s: topk %d", who, topk);
   if (T == 0) {
@@ -405,16 +424,20 @@ int dsv4_sparse_prefill_attn(const void* q, int64_t T, int64_t q_pos0, int32_t n
 
 // Bytes of narrow-attention workspace for T queries split n_splits ways:
 // fp32 O [T][n_splits][n_heads][head_dim], then (m, l) [T][n_splits][n_heads][2].
-static size_t narrow_ws_bytes(int64_t T, int32_t n_splits, int32_t n_heads, int32_t head_dim) {
-  return static_cast<size_t>(T) * static_cast<size_t>(n_splits) * static_cast<size_t>(n_heads) *
-         (static_cast<size_t>(head_dim) + 2) * sizeof(float);
+// False when the size does not fit a size_t.
+static bool narrow_ws_bytes(int64_t T, int32_t n_splits, int32_t n_heads, int32_t head_dim,
+                            size_t* bytes) {
+  size_t n = 0;
+  return mul_size(static_cast<size_t>(T), static_cast<size_t>(n_splits), &n) &&
+         mul_size(n, static_cast<size_t>(n_heads), &n) &&
+         mul_size(n, (static_cast<size_t>(head_dim) + 2) * sizeof(float), bytes);
 }
 
 int dsv4_sparse_attn_narrow_plan(int64_t T, int32_t n_heads, int32_t head_dim, int32_t window,
                                  int64_t n_pooled_keys, int32_t* n_splits,
                                  size_t* workspace_bytes) {
-  if (!n_splits || !workspace_bytes || T < 0 || n_heads < 1 || head_dim < 1 || window < 1 ||
-      n_pooled_keys < 0)
+  if (!n_splits || !workspace_bytes || !extent_ok(T) || n_heads < 1 || n_heads > DSV4_MAX_HEADS ||
+      head_dim < 1 || head_dim > 512 || window < 1 || !extent_ok(n_pooled_keys))
     return fail(DSV4_ERR_INVALID_ARG, "sparse_attn_narrow_plan: bad arguments");
   // About one workgroup per CU in all (256), each with at least two 32-key
   // tiles, at most DSV4_MAX_ATTN_SPLITS splits.
@@ -423,8 +446,11 @@ int dsv4_sparse_attn_narrow_plan(int64_t T, int32_t n_heads, int32_t head_dim, i
   if (ns > tiles / 2) ns = tiles / 2;
   if (ns > DSV4_MAX_ATTN_SPLITS) ns = DSV4_MAX_ATTN_SPLITS;
   if (ns < 1) ns = 1;
+  size_t ws = 0;
+  if (ns > 1 && !narrow_ws_bytes(T, static_cast<int32_t>(ns), n_heads, head_dim, &ws))
+    return fail(DSV4_ERR_INVALID_ARG, "sparse_attn_narrow_plan: workspace overflows size_t");
   *n_splits = static_cast<int32_t>(ns);
-  *workspace_bytes = ns > 1 ? narrow_ws_bytes(T, *n_splits, n_heads, head_dim) : 0;
+  *workspace_bytes = ws;
   return DSV4_OK;
 }
 
@@ -443,7 +469,9 @@ int dsv4_sparse_attn_narrow(const void* q, int64_t T, int64_t q_pos0, int32_t n_
   float* part_o = nullptr;
   float* part_ml = nullptr;
   if (n_splits > 1) {
-    const size_t need = narrow_ws_bytes(T, n_splits, n_heads, head_dim);
+    size_t need = 0;
+    if (!narrow_ws_bytes(T, n_splits, n_heads, head_dim, &need))
+      return fail(DSV4_ERR_INVALID_ARG, "sparse_attn_narrow: workspace overflows size_t");
     if (!workspace || !aligned16(workspace))
       return fail(DSV4_ERR_INVALID_ARG, "sparse_attn_narrow: workspace NULL or not 16-byte aligned");
     if (workspace_bytes < need)

@@ -60,21 +60,21 @@ extern "C" int dsv4_indexer_select_noalloc(const dsv4_pool_cache* index_cache,
   if (T < 0 || tile_rows < 0)
     return dsv4_internal_fail(DSV4_ERR_INVALID_ARG, "indexer_select_noalloc: negative size");
   const int64_t S = index_cache->n_rows;
-  const size_t row_bytes = static_cast<size_t>(dsv4_score_stride(S)) * sizeof(float);
+  // the full path (the others need no scratch); a pool count outside
+  // [0, DSV4_MAX_EXTENT] takes no scratch and fails the cache checks below
+  const bool scores = T > 0 && S > topk && S <= DSV4_MAX_EXTENT;
+  const size_t row_bytes =
+      scores ? static_cast<size_t>(dsv4_score_stride(S)) * sizeof(float) : sizeof(float);
   const size_t cap = DSV4_NOALLOC_SCRATCH_BYTES;
-  const bool scores = T > 0 && S > topk;  // the full path (others need no scratch)
+  const int64_t fit = static_cast<int64_t>(cap / row_bytes);  // score rows the array holds
   int64_t tile = (tile_rows == 0 || tile_rows > T) ? T : tile_rows;
-  if (scores && tile_rows == 0) {
-    const int64_t fit = static_cast<int64_t>(cap / row_bytes);
-    if (fit < tile) tile = fit;
-  }
-  if (scores && (tile < 1 || static_cast<size_t>(tile) * row_bytes > cap))
+  if (scores && tile_rows == 0 && fit < tile) tile = fit;
+  if (scores && (tile < 1 || tile > fit))
     return dsv4_internal_fail(DSV4_ERR_SCRATCH,
-                              "indexer_select_noalloc: a %lld-row tile of %lld pooled rows needs "
-                              "%zu bytes, the static scratch holds %zu",
+                              "indexer_select_noalloc: a %lld-row tile of %lld pooled rows does "
+                              "not fit the static scratch of %zu bytes (%lld rows of them do)",
                               static_cast<long long>(tile < 1 ? 1 : tile),
-                              static_cast<long long>(S),
-                              static_cast<size_t>(tile < 1 ? 1 : tile) * row_bytes, cap);
+                              static_cast<long long>(S), cap, static_cast<long long>(fit));
   void* p = nullptr;
   if (scores) {
     const int rc = device_scratch(&p);

@@ -40,7 +40,7 @@ def test_use_library_switches_and_restores():
 
 
 def test_abi_version_and_host_helpers():
-    assert dsv4.dsv4_abi_version() == 5
+    assert dsv4.dsv4_abi_version() == 6
     assert dsv4.dsv4_indexer_all_pooled(0, 8) is False
     assert dsv4.dsv4_indexer_all_pooled(1, 8) is True
     assert dsv4.dsv4_indexer_all_pooled(8, 8) is True
