@@ -20,7 +20,8 @@ __all__ = [
     "dsv4_indexer_scratch_bytes", "dsv4_compress", "dsv4_indexer_scores", "dsv4_topk_select",
     "dsv4_indexer_select", "dsv4_sparse_prefill_attn", "dsv4_sparse_attn_narrow_plan",
     "dsv4_sparse_attn_narrow", "dsv4_topk_split_workspace_bytes", "dsv4_topk_select_split",
-    "dsv4_indexer_select_noalloc", "DSV4_NOALLOC_SCRATCH_BYTES", "use_library",
+    "dsv4_indexer_select_noalloc", "DSV4_NOALLOC_SCRATCH_BYTES", "DSV4_MAX_EXTENT",
+    "use_library",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +31,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "dsv4.h")
 DSV4_BF16 = 1
 DSV4_F32 = 2
 DSV4_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
+DSV4_MAX_EXTENT = 1 << 40  # largest position / count / size / stride any call takes
 RATIO = 4
 
 c_i32, c_i64, c_vp, c_f32, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t

@@ -49,6 +49,29 @@ def test_abi_version_and_host_helpers():
     assert dsv4.dsv4_score_stride(65) == 128
     # one 1,024-row tile against 262,144 pooled rows: 1 GiB of fp32 scores
     assert dsv4.dsv4_indexer_scratch_bytes(1024, 262144) == 1 << 30
+    # past the extent bound: -1, and sizes past it are refused
+    ext = dsv4.DSV4_MAX_EXTENT
+    assert dsv4.dsv4_score_stride(ext) == ext and dsv4.dsv4_score_stride(ext + 1) == -1
+    with pytest.raises(dsv4.DSV4Error):
+        dsv4.dsv4_indexer_scratch_bytes(1, ext + 1)
+    with pytest.raises(dsv4.DSV4Error):  # 2^40 x 2^40 x 4 bytes do not fit a size_t
+        dsv4.dsv4_indexer_scratch_bytes(ext, ext)
+
+
+def test_binding_constants_match_header():
+    """The binding's copies of the header's constants, read from the header."""
+    import re
+    text = open(dsv4.HEADER_PATH).read()
+
+    def define(name):
+        m = re.search(r"#define\s+%s\s+(.+)" % name, text)
+        expr = re.sub(r"\(int64_t\)|(?<=\d)u\b", "", m.group(1).split("/*")[0])
+        return eval(expr, {"__builtins__": {}})
+
+    assert dsv4.DSV4_NOALLOC_SCRATCH_BYTES == define("DSV4_NOALLOC_SCRATCH_BYTES")
+    assert dsv4.DSV4_MAX_EXTENT == define("DSV4_MAX_EXTENT")
+    assert dsv4.dsv4_abi_version() == define("DSV4_ABI_VERSION")
+    assert (dsv4.DSV4_BF16, dsv4.DSV4_F32) == (define("DSV4_BF16"), define("DSV4_F32"))
 
 
 def _cache(n_rows=0, n_rem=0, cap=16, dim=128, dtype=1, ratio=4, rows=FAKE, rem=FAKE):
