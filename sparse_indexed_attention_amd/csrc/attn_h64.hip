@@ -476,6 +476,7 @@ hipError_t dsv4_launch_sparse_attn_h64(const void* q, int64_t T, int64_t q_pos0,
                                        const void* pooled, int32_t ratio, const int32_t* sel_idx,
                                        int32_t topk, void* out, int32_t nsplit, float* part_o,
                                        float* part_ml, hipStream_t s) {
+  if (!dispatch_fits(T, kNT)) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>(nsplit));
   const size_t dyn = static_cast<size_t>(sel_idx ? topk : 0) * sizeof(int);
   hipLaunchKernelGGL(attn_h64_kernel, grid, dim3(kNT), dyn, s, static_cast<const uint16_t*>(q),

@@ -119,6 +119,13 @@ __device__ __forceinline__ void global_to_lds4(const void* g, const void* lds_wa
                : "memory");
 }
 
+// Whether `blocks` workgroups of `threads` work-items fit one dispatch along
+// x: the dispatch packet counts work-items in 32 bits, so a larger count
+// would otherwise be cut short when it becomes a grid size.
+inline bool dispatch_fits(int64_t blocks, int64_t threads) {
+  return blocks >= 1 && threads >= 1 && blocks <= int64_t(0xFFFFFFFF) / threads;
+}
+
 // s_waitcnt immediates (gfx9 encoding): vmcnt(n) with the other counters open,
 // and lgkmcnt(0) with the others open.
 constexpr int kWaitVm0 = 0x0F70;

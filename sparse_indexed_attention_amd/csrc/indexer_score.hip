@@ -368,6 +368,7 @@ hipError_t launch_t(const void* q, const float* w, const void* keys, int64_t row
   int64_t cps = (S + splits - 1) / splits;
   cps = (cps + kTileCols - 1) / kTileCols * kTileCols;
   const int64_t grid = 8 * per_cg * nqb_g;
+  if (!dispatch_fits(grid, kThreads)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((indexer_score_kernel<KSTEPS, MT>), dim3(static_cast<unsigned>(grid)),
                      dim3(kThreads), 0, s, static_cast<const uint16_t*>(q), w,
                      static_cast<const uint16_t*>(keys), rows, q_pos0, S, n_heads, fold_mask,

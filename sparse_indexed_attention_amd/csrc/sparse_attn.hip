@@ -500,6 +500,7 @@ hipError_t launch_d(const void* q, int64_t T, int64_t q_pos0, int H, float sl2, 
                     int64_t raw_pos0, int window, const void* pooled, int ratio,
                     const int32_t* sel, int topk, void* out, int nsplit, float* part_o,
                     float* part_ml, hipStream_t s) {
+  if (!dispatch_fits(T, 512)) return hipErrorInvalidValue;  // at most 512 work-items each
   const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>(nsplit));
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* rr = static_cast<const uint16_t*>(raw);
@@ -580,7 +581,8 @@ hipError_t dsv4_launch_attn_combine(const float* part_o, const float* part_ml, i
                                     int32_t nsplit, int32_t n_heads, int32_t head_dim, void* out,
                                     hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (nsplit > kMaxAttnSplits || head_dim % 4 != 0 || head_dim > 1024) return hipErrorInvalidValue;
+  if (nsplit > kMaxAttnSplits || head_dim % 4 != 0 || head_dim > 1024 || !dispatch_fits(T, 256))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<unsigned>(T), static_cast<unsigned>(n_heads)),
                      dim3(256), 0, s, part_o, part_ml, nsplit, n_heads, head_dim,
                      static_cast<uint16_t*>(out));

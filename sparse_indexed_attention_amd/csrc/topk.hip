@@ -1189,6 +1189,8 @@ hipError_t launch_reg(RegArgs a, int64_t max_cols, hipStream_t s) {
   if (PASS != kRegChunk && max_cols <= 64 * 64 && !two_short) {
     // one wave per item, kShortWaves items per workgroup; per wave the
     // histogram, later the chosen columns + 64 spare slots (16-bit)
+    if (!dispatch_fits((items + kShortWaves - 1) / kShortWaves, 64 * kShortWaves))
+      return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>((items + kShortWaves - 1) / kShortWaves));
     const dim3 block(64 * kShortWaves);
     int words = (a.cap + 64 + 1) / 2;
@@ -1209,6 +1211,7 @@ hipError_t launch_reg(RegArgs a, int64_t max_cols, hipStream_t s) {
   // slots, inside the 2 x kBins words)
   a.words = 2 * kBins;
   const size_t lds = static_cast<size_t>(a.words) * sizeof(uint32_t);
+  if (!dispatch_fits(items, 512)) return hipErrorInvalidValue;  // at most 8 waves each
   const dim3 grid(static_cast<unsigned>(items));
   constexpr int P2 = PASS == kRegChunk ? kRegRows : PASS;  // chunk items take 8 waves
   if (PASS == kRegChunk || max_cols > 4 * 64 * 64)
