@@ -441,6 +441,30 @@ def test_topk_tie_heavy_long_rows(levels):
     np.testing.assert_array_equal(got, O.topk_select(s.astype(np.float64), q_pos0, topk))
 
 
+@pytest.mark.parametrize("T,q_pos0,W,topk", [
+    (70, 0, 128, 2048),   # the stream's first tokens: clipped window, 0-17 pooled rows
+    (1, 5000, 128, 4096), # the largest k, more slots than visible rows (1,250)
+    (5, 130, 128, 1),     # a single slot
+    (3, 10, 1, 64),       # a one-token window, mostly empty selections
+    (33, 127, 128, 64),   # the first query whose window is full, ragged tile tail
+])
+def test_attention_hot_shape_edges(T, q_pos0, W, topk):
+    """The H = 64, D = 512 shape at its edges: positions from 0, windows cut
+    at the stream start, k = 1 and k = DSV4_MAX_TOPK, selections mostly empty
+    (every slot a query cannot see is -1 or a decoy row beyond visibility)."""
+    H, D = 64, 512
+    cache, pooled, raw, raw_pos0, q, sel = _attn_case(T, q_pos0, H, D, W, topk,
+                                                      seed=9000 + T + q_pos0 + topk)
+    out = torch.zeros((T, H, D), dtype=torch.bfloat16, device="cuda")
+    dsv4.dsv4_sparse_prefill_attn(bf16_t(q.reshape(T, H * D)).cuda().view(T, H, D), q_pos0,
+                                  bf16_t(raw).cuda(), raw_pos0, W, cache,
+                                  torch.from_numpy(sel).cuda(), out)
+    torch.cuda.synchronize()
+    ref = O.sparse_prefill_attention(q, q_pos0, raw, raw_pos0, W, pooled, sel, 1 / math.sqrt(D))
+    err = np.abs(out.float().cpu().numpy() - ref).max()
+    assert err <= ATTN_ATOL, err
+
+
 def test_attention_unsorted_and_duplicate_selections():
     """Selections the indexer never makes but the ABI accepts: slots in
     descending order and repeated rows.  Each listed slot is a key, as in the
