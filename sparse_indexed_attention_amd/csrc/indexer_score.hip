@@ -34,9 +34,10 @@
 //     column with the query's visible count.
 //   * Software pipeline: a 32-column block runs 2*MT accumulation chains of
 //     KSTEPS MFMAs; the epilogue of each chain is issued under the next
-//     chain's MFMAs, and the last chain's epilogue plus the block's store move
-//     into the next block (across the tile barrier), so the matrix pipe has
-//     independent work beside every epilogue.  The block body has no branches:
+//     chain's MFMAs (after the first two of them, which cover the wait for
+//     its accumulator), and the last chain's epilogue plus the block's store
+//     move into the next block (across the tile barrier), so the matrix pipe
+//     has independent work beside every epilogue.  The block body has no branches:
 //     stores go through a buffer resource whose range check drops lanes whose
 //     column or query is out of range.
 //   * Four-wave workgroups, two per CU: their barriers are independent, so one
@@ -273,6 +274,21 @@ indexer_score_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w
         epilogue(prev, c - 1, part[(c - 1) / MT]);
       }
       prev = acc;
+      if (c >= 1) {
+        // Issue order of this region (masks: 0x008 MFMA, 0x002 VALU): two of
+        // this chain's MFMAs first, while the previous chain's accumulator
+        // settles, then its epilogue spread five VALU to an MFMA over the
+        // other six.  Left to itself the scheduler opens the region with the
+        // epilogue, whose first reads wait on that accumulator with the
+        // matrix pipe idle.
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+#pragma unroll
+        for (int g = 0; g < KSTEPS - 2; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
+      }
       // one chain's MFMAs beside one epilogue: keeps two accumulators live
       __builtin_amdgcn_sched_barrier(0);
     }
