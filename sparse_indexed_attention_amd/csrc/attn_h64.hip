@@ -29,8 +29,10 @@
 // costs one more barrier.  Otherwise p <= 2^8.
 // Pipeline, one barrier per tile over four LDS stages: P, the tile maxima
 // and the flags are double-buffered by tile parity, so after the barrier of
-// tile t a wave runs P.V(t-1), QK(t) and softmax(t) with no barrier between
-// them, while the gathers of tiles t+1 and t+2 are in flight.
+// tile t a wave runs QK(t), P.V(t-1) and softmax(t) with no barrier between
+// them, while the gathers of tiles t+1 and t+2 are in flight.  QK comes
+// first so that P.V's MFMAs, not a stall, separate its last MFMA from the
+// softmax's first read of its result.
 #include <type_traits>
 
 #include "dsv4_device.h"
@@ -312,13 +314,13 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
     // it % 2 of P, the tile maxima and the flags follows):
     //   wait for tile it's rows; the barrier (tile it, P(it-1), the maxima
     //   and flags of it-1; stage it-2 and the parity-it buffers are free);
-    //   gather tile it+2; settle the flags of it-1 (owners move references,
-    //   rewrite P(it-1), publish factors; one more barrier, rare); then
-    //   P.V(it-1), QK(it) and softmax(it) -> P(it), which need no barrier
-    //   between them.
+    //   gather tile it+2; QK(it); settle the flags of it-1 (owners move
+    //   references, rewrite P(it-1), publish factors; one more barrier,
+    //   rare); then P.V(it-1) and softmax(it) -> P(it), which need no
+    //   barrier between them.
     // `kind` 0 is the first tile (no P.V, no flags), 1 a middle tile
     // (1 <= it < n_tiles), 2 the final pass (it = n_tiles: P.V only); the
-    // middle tiles carry no tile-count tests around P.V, QK and softmax, so
+    // middle tiles carry no tile-count tests around QK, P.V and softmax, so
     // those are one basic block the compiler can interleave.
     auto step = [&](auto st, auto kind_c, int it) {
       constexpr int S = decltype(st)::value;
@@ -340,6 +342,10 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
         vm_after = static_cast<uint32_t>(lk.valid >> (32 * (S & 1)));
         if ((S & 1) && it + 3 < n_tiles) lk = lookup(tile_lo + it + 3);
       }
+      // QK(it) first: its MFMAs are done by the time the softmax reads them,
+      // P.V(it-1) issuing in between
+      f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (has_qk) sc = qk(std::integral_constant<int, S>{});
       if constexpr (has_pv) {
         // ---- flags of tile it-1: move the references where a tile max
         // passed them by more than the slack (uniform decision)
@@ -369,9 +375,8 @@ attn_h64_kernel(const uint16_t* __restrict__ q, int64_t q_pos0, float scale_log2
         pv(std::integral_constant<int, SP>{}, std::integral_constant<int, PARP>{});
       }
       if constexpr (has_qk) {
-        // ---- QK(it) and the softmax of the owned (head tile, key half):
+        // ---- the softmax of the owned (head tile, key half):
         // rows 4 kb + i are keys 16 kh + 4 i + kb
-        const f32x4_t sc = qk(std::integral_constant<int, S>{});
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
